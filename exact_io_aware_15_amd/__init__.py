@@ -1,0 +1,159 @@
+"""Exact attention (FlashAttention forward) and paged-KV decode for MI355X (gfx950).
+
+Thin ctypes binding over libfa.so, whose C ABI is declared in include/fa.h.  The
+functions below carry the C names and only marshal arguments: they check dtypes,
+shapes, contiguity and devices, allocate outputs with torch when none are given,
+and pass raw device pointers plus torch's current HIP stream.  Every step of the
+computation runs in the library's HIP kernels; there is no fallback path, and a
+missing library raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+__all__ = [
+    "FAError",
+    "lib",
+    "fa_fwd",
+    "fa_fwd_f32",
+    "fa_decode_paged",
+    "fa_decode_paged_workspace_size",
+    "fa_status_string",
+    "LIB_PATH",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
+
+FA_OK = 0
+_lib = None
+
+
+class FAError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: status {status}: {fa_status_string(status)}")
+
+
+def lib() -> ctypes.CDLL:
+    """Load libfa.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m exact_io_aware_15_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    L.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp]
+    L.fa_fwd.restype = i
+    L.fa_fwd_f32.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp]
+    L.fa_fwd_f32.restype = i
+    L.fa_decode_paged_workspace_size.argtypes = [i, i, i, i, i]
+    L.fa_decode_paged_workspace_size.restype = sz
+    L.fa_decode_paged.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp, sz, vp]
+    L.fa_decode_paged.restype = i
+    L.fa_status_string.argtypes = [i]
+    L.fa_status_string.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def fa_status_string(status: int) -> str:
+    return lib().fa_status_string(int(status)).decode()
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _need(t: torch.Tensor, name: str, dtype, shape, device):
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    if t.device != device:
+        raise ValueError(f"{name}: on {t.device}, expected {device}")
+
+
+def _fwd(entry: str, dtype, q, k, v, causal, scale, out, lse):
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q must be [B, Hq, N, d] and k, v [B, Hkv, N, d]")
+    B, Hq, N, d = q.shape
+    Hkv = k.shape[1]
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on a GPU")
+    _need(q, "q", dtype, (B, Hq, N, d), dev)
+    _need(k, "k", dtype, (B, Hkv, N, d), dev)
+    _need(v, "v", dtype, (B, Hkv, N, d), dev)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((B, Hq, N, d), dtype=dtype, device=dev)
+    if lse is None:
+        lse = torch.empty((B, Hq, N), dtype=torch.float32, device=dev)
+    _need(out, "out", dtype, (B, Hq, N, d), dev)
+    _need(lse, "lse", torch.float32, (B, Hq, N), dev)
+    st = getattr(lib(), entry)(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv, N, d,
+                               int(bool(causal)), float(scale), _stream(q))
+    if st != FA_OK:
+        raise FAError(st, entry)
+    return out, lse
+
+
+def fa_fwd(q, k, v, causal=False, scale=None, out=None, lse=None):
+    """bf16 forward: q [B,Hq,N,d], k/v [B,Hkv,N,d] -> (O bf16 [B,Hq,N,d], L fp32 [B,Hq,N])."""
+    return _fwd("fa_fwd", torch.bfloat16, q, k, v, causal, scale, out, lse)
+
+
+def fa_fwd_f32(q, k, v, causal=False, scale=None, out=None, lse=None):
+    """fp32 forward, same layouts as fa_fwd."""
+    return _fwd("fa_fwd_f32", torch.float32, q, k, v, causal, scale, out, lse)
+
+
+def fa_decode_paged_workspace_size(num_seqs, Hq, d, max_pages_per_seq, page_size=16) -> int:
+    return int(lib().fa_decode_paged_workspace_size(num_seqs, Hq, d, max_pages_per_seq, page_size))
+
+
+def fa_decode_paged(q, kpages, vpages, page_table, ctx_lens, scale=None, out=None, lse=None,
+                    workspace=None):
+    """Paged decode: q [S,Hq,d] bf16; kpages/vpages [P,Hkv,16,d] bf16; page_table [S,maxp] int32;
+    ctx_lens [S] int32 -> (O bf16 [S,Hq,d], L fp32 [S,Hq])."""
+    S, Hq, d = q.shape
+    P, Hkv, page_size, dk = kpages.shape
+    maxp = page_table.shape[1]
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on a GPU")
+    _need(q, "q", torch.bfloat16, (S, Hq, d), dev)
+    _need(kpages, "kpages", torch.bfloat16, (P, Hkv, page_size, d), dev)
+    _need(vpages, "vpages", torch.bfloat16, (P, Hkv, page_size, d), dev)
+    _need(page_table, "page_table", torch.int32, (S, maxp), dev)
+    _need(ctx_lens, "ctx_lens", torch.int32, (S,), dev)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((S, Hq, d), dtype=torch.bfloat16, device=dev)
+    if lse is None:
+        lse = torch.empty((S, Hq), dtype=torch.float32, device=dev)
+    _need(out, "out", torch.bfloat16, (S, Hq, d), dev)
+    _need(lse, "lse", torch.float32, (S, Hq), dev)
+    need = fa_decode_paged_workspace_size(S, Hq, d, maxp, page_size)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    st = lib().fa_decode_paged(_ptr(q), _ptr(kpages), _ptr(vpages), _ptr(page_table), _ptr(ctx_lens),
+                               _ptr(out), _ptr(lse), S, Hq, Hkv, d, page_size, maxp, P, float(scale),
+                               _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(q))
+    if st != FA_OK:
+        raise FAError(st, "fa_decode_paged")
+    return out, lse

@@ -1,0 +1,294 @@
+// Split-K paged-KV decode: one query token per sequence attends its whole
+// cached context, which lives in fixed 16-token pages reached through a page
+// table ("Phase 08 -- Inference Optimization at Depth", Concepts list: KV cache,
+// paged attention; Lab 03 steps 1 and 4).
+//
+// Phase 1 (decode_split_kernel): one workgroup per (split of 32 pages, K/V head,
+// sequence) serves up to HB query heads of that K/V head's group, so each K/V
+// page is read from HBM once for the whole group.  Its 4 waves take the split's
+// pages round-robin.  In a wave, lane l holds tokens 2*(l/8) and 2*(l/8)+1 of
+// the page and the d columns {8*(l%8) + 64*c .. +8}; each (page, head) block is
+// 4 KB contiguous, so every 16-byte load instruction covers 8 whole 128-byte
+// row segments.  The next page is fetched while the current one is consumed.
+// Scores: per-lane FMAs then a 3-step DPP sum over the 8 lanes of a token.  The
+// wave keeps the online-softmax state (running max m, sum l, unnormalised
+// accumulator) of the "Phase 08" Lab 01 recurrence, rescaling only when a head's
+// max grows.  Tokens at or past ctx_len get probability 0 and their V rows are
+// zeroed before use, so NaN in unused slots cannot leak (0 * NaN).  The waves'
+// states are merged through LDS and the split writes (o_c normalised, lse_c).
+//
+// Phase 2 (decode_merge_kernel): per (sequence, query head) combine the splits:
+// L = log sum_c exp(lse_c), O = sum_c exp(lse_c - L) o_c.
+#include "fa_device.h"
+#include "fa_launch.h"
+
+namespace fa {
+namespace {
+
+constexpr int kPage = 16;
+constexpr int kDecWaves = 4;
+constexpr int kDecThreads = kDecWaves * 64;
+
+__device__ __forceinline__ u32x4 ldg16(const uint16_t* p) { return *reinterpret_cast<const u32x4*>(p); }
+
+template <int D, int HB>
+__global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ KPg, const uint16_t* __restrict__ VPg,
+    const int32_t* __restrict__ table, const int32_t* __restrict__ ctx, float* __restrict__ ws_o,
+    float* __restrict__ ws_l, int Hq, int Hkv, int max_pages, int max_splits, int nhb, float c) {
+  constexpr int CPL = D / 64;  // 8-column chunks per token per lane
+  constexpr int DL = CPL * 8;  // d columns per lane
+  __shared__ float sm_m[kDecWaves][HB];
+  __shared__ float sm_l[kDecWaves][HB];
+  __shared__ float sm_acc[kDecWaves][HB][D];
+
+  const int split = blockIdx.x;
+  const int g = blockIdx.y / nhb;
+  const int hb = blockIdx.y % nhb;
+  const int s = blockIdx.z;
+  const int G = Hq / Hkv;
+  const int n = ctx[s];
+  const int npages = (n + kPage - 1) / kPage;
+  const int p_begin = split * kDecodePagesPerSplit;
+  if (p_begin >= npages) return;  // this split has no tokens: nothing is written or read later
+  const int p_end = min(npages, p_begin + kDecodePagesPerSplit);
+
+  const int tid = threadIdx.x;
+  const int w = tid >> 6;
+  const int lane = tid & 63;
+  const int tg = lane >> 3;  // token pair within the page
+  const int dg = lane & 7;   // column group
+
+  // query heads served: h = g*G + hb*HB + hh, valid while hb*HB + hh < G
+  float qv[HB][DL];
+#pragma unroll
+  for (int hh = 0; hh < HB; ++hh) {
+    const int hl = hb * HB + hh;
+    const bool ok = hl < G;
+    const uint16_t* qp = Q + ((size_t)s * Hq + g * G + (ok ? hl : 0)) * D;
+#pragma unroll
+    for (int cc = 0; cc < CPL; ++cc) {
+      u32x4 x = ldg16(qp + (dg + 8 * cc) * 8);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        qv[hh][cc * 8 + 2 * e] = ok ? bf16lo_to_f32(x[e]) * c : 0.f;
+        qv[hh][cc * 8 + 2 * e + 1] = ok ? bf16hi_to_f32(x[e]) * c : 0.f;
+      }
+    }
+  }
+
+  float m_run[HB], l_run[HB], acc[HB][DL];
+#pragma unroll
+  for (int hh = 0; hh < HB; ++hh) {
+    m_run[hh] = -INFINITY;
+    l_run[hh] = 0.f;
+#pragma unroll
+    for (int i = 0; i < DL; ++i) acc[hh][i] = 0.f;
+  }
+
+  const int32_t* trow = table + (size_t)s * max_pages;
+  const size_t head_off = (size_t)g * kPage * D;
+  const size_t page_stride = (size_t)Hkv * kPage * D;
+
+  u32x4 kc[2][CPL], vc[2][CPL];  // current page
+  u32x4 kn[2][CPL], vn[2][CPL];  // next page
+  auto fetch = [&](int p, u32x4 (&kd)[2][CPL], u32x4 (&vd)[2][CPL]) {
+    const size_t base = (size_t)trow[p] * page_stride + head_off;
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int cc = 0; cc < CPL; ++cc) {
+        const size_t off = base + (size_t)(2 * tg + j) * D + (dg + 8 * cc) * 8;
+        kd[j][cc] = ldg16(KPg + off);
+        vd[j][cc] = ldg16(VPg + off);
+      }
+  };
+
+  int p = p_begin + w;
+  if (p < p_end) fetch(p, kc, vc);
+  for (; p < p_end; p += kDecWaves) {
+    const int pn = p + kDecWaves;
+    if (pn < p_end) fetch(pn, kn, vn);
+
+    // scores for this lane's two tokens, every served head
+    float sc[2][HB];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int tok = p * kPage + 2 * tg + j;
+      const bool valid = tok < n;
+#pragma unroll
+      for (int hh = 0; hh < HB; ++hh) {
+        float part = 0.f;
+#pragma unroll
+        for (int cc = 0; cc < CPL; ++cc)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            part = __builtin_fmaf(qv[hh][cc * 8 + 2 * e], bf16lo_to_f32(kc[j][cc][e]), part);
+            part = __builtin_fmaf(qv[hh][cc * 8 + 2 * e + 1], bf16hi_to_f32(kc[j][cc][e]), part);
+          }
+        part = sum8(part);
+        sc[j][hh] = valid ? part : -INFINITY;
+      }
+    }
+    // online softmax state update (wave-uniform max per head)
+    bool grow = false;
+    float mnew[HB];
+#pragma unroll
+    for (int hh = 0; hh < HB; ++hh) {
+      const float pm = max_stride8(fmaxf(sc[0][hh], sc[1][hh]));
+      mnew[hh] = fmaxf(m_run[hh], pm);
+      grow |= mnew[hh] > m_run[hh];
+    }
+    if (grow) {
+#pragma unroll
+      for (int hh = 0; hh < HB; ++hh) {
+        const float alpha = exp2_fast(m_run[hh] - mnew[hh]);
+        l_run[hh] *= alpha;
+#pragma unroll
+        for (int i = 0; i < DL; ++i) acc[hh][i] *= alpha;
+        m_run[hh] = mnew[hh];
+      }
+    }
+    // the last page may hold slots past ctx_len: zero their V so 0 * NaN cannot occur
+    if ((p + 1) * kPage > n) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const bool valid = p * kPage + 2 * tg + j < n;
+#pragma unroll
+        for (int cc = 0; cc < CPL; ++cc)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) vc[j][cc][e] = valid ? vc[j][cc][e] : 0u;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int hh = 0; hh < HB; ++hh) {
+        const float pr = (sc[j][hh] == -INFINITY) ? 0.f : exp2_fast(sc[j][hh] - m_run[hh]);
+        l_run[hh] += pr;
+#pragma unroll
+        for (int cc = 0; cc < CPL; ++cc)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            acc[hh][cc * 8 + 2 * e] = __builtin_fmaf(pr, bf16lo_to_f32(vc[j][cc][e]), acc[hh][cc * 8 + 2 * e]);
+            acc[hh][cc * 8 + 2 * e + 1] =
+                __builtin_fmaf(pr, bf16hi_to_f32(vc[j][cc][e]), acc[hh][cc * 8 + 2 * e + 1]);
+          }
+      }
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int cc = 0; cc < CPL; ++cc) {
+        kc[j][cc] = kn[j][cc];
+        vc[j][cc] = vn[j][cc];
+      }
+  }
+
+  // combine the 8 token-pair lanes of each column group, then the 4 waves
+#pragma unroll
+  for (int hh = 0; hh < HB; ++hh) {
+    l_run[hh] = sum_stride8(l_run[hh]);
+#pragma unroll
+    for (int i = 0; i < DL; ++i) acc[hh][i] = sum_stride8(acc[hh][i]);
+  }
+  if (lane < 8) {
+#pragma unroll
+    for (int hh = 0; hh < HB; ++hh) {
+      if (lane == 0) {
+        sm_m[w][hh] = m_run[hh];
+        sm_l[w][hh] = l_run[hh];
+      }
+#pragma unroll
+      for (int cc = 0; cc < CPL; ++cc)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sm_acc[w][hh][(dg + 8 * cc) * 8 + e] = acc[hh][cc * 8 + e];
+    }
+  }
+  __syncthreads();
+  for (int i = tid; i < HB * D; i += kDecThreads) {
+    const int hh = i / D, d = i % D;
+    const int hl = hb * HB + hh;
+    if (hl >= G) continue;
+    float M = -INFINITY;
+#pragma unroll
+    for (int ww = 0; ww < kDecWaves; ++ww) M = fmaxf(M, sm_m[ww][hh]);
+    float wsum = 0.f, o = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < kDecWaves; ++ww) {
+      const float mw = sm_m[ww][hh];
+      const float f = (mw == -INFINITY) ? 0.f : exp2_fast(mw - M);
+      wsum += f * sm_l[ww][hh];
+      o += f * sm_acc[ww][hh][d];
+    }
+    const size_t slot = ((size_t)s * Hq + g * G + hl) * max_splits + split;
+    ws_o[slot * D + d] = o / wsum;
+    if (d == 0) ws_l[slot] = M + log2_fast(wsum);  // log2 units
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(D) void decode_merge_kernel(const float* __restrict__ ws_o,
+                                                         const float* __restrict__ ws_l,
+                                                         const int32_t* __restrict__ ctx,
+                                                         uint16_t* __restrict__ O, float* __restrict__ Lse,
+                                                         int Hq, int max_splits) {
+  const int s = blockIdx.x / Hq;
+  const int h = blockIdx.x % Hq;
+  const int d = threadIdx.x;
+  const int n = ctx[s];
+  const size_t out = ((size_t)s * Hq + h);
+  if (n <= 0) {
+    O[out * D + d] = 0;
+    if (d == 0) Lse[out] = -INFINITY;
+    return;
+  }
+  const int nsplit = ((n + kPage - 1) / kPage + kDecodePagesPerSplit - 1) / kDecodePagesPerSplit;
+  const float* lp = ws_l + out * max_splits;
+  const float* op = ws_o + out * max_splits * D;
+  float M = -INFINITY;
+  for (int c = 0; c < nsplit; ++c) M = fmaxf(M, lp[c]);
+  float wsum = 0.f, o = 0.f;
+  for (int c = 0; c < nsplit; ++c) {
+    const float f = exp2_fast(lp[c] - M);
+    wsum += f;
+    o += f * op[(size_t)c * D + d];
+  }
+  O[out * D + d] = __builtin_bit_cast(uint16_t, to_bf16(o / wsum));
+  if (d == 0) Lse[out] = (M + log2_fast(wsum)) * kLn2;
+}
+
+template <int D, int HB>
+hipError_t launch_split(const DecodeArgs& a, float* ws_o, float* ws_l, int max_splits) {
+  const int G = a.Hq / a.Hkv;
+  const int nhb = (G + HB - 1) / HB;
+  const dim3 grid((unsigned)max_splits, (unsigned)(a.Hkv * nhb), (unsigned)a.S);
+  hipLaunchKernelGGL((decode_split_kernel<D, HB>), grid, dim3(kDecThreads), 0, (hipStream_t)a.stream,
+                     (const uint16_t*)a.q, (const uint16_t*)a.kpages, (const uint16_t*)a.vpages, a.page_table,
+                     a.ctx_lens, ws_o, ws_l, a.Hq, a.Hkv, a.max_pages, max_splits, nhb, a.scale * kLog2e);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_d(const DecodeArgs& a) {
+  const int max_splits = decode_max_splits(a.max_pages);
+  float* ws_o = (float*)a.workspace;
+  const size_t o_bytes = (size_t)a.S * a.Hq * max_splits * D * sizeof(float);
+  float* ws_l = (float*)((uint8_t*)a.workspace + ((o_bytes + 255) / 256) * 256);
+  const int G = a.Hq / a.Hkv;
+  hipError_t e;
+  if (G <= 1) e = launch_split<D, 1>(a, ws_o, ws_l, max_splits);
+  else if (G <= 2) e = launch_split<D, 2>(a, ws_o, ws_l, max_splits);
+  else e = launch_split<D, 4>(a, ws_o, ws_l, max_splits);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((decode_merge_kernel<D>), dim3((unsigned)(a.S * a.Hq)), dim3(D), 0, (hipStream_t)a.stream,
+                     ws_o, ws_l, a.ctx_lens, (uint16_t*)a.o, a.lse, a.Hq, max_splits);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_decode_paged(const DecodeArgs& a) {
+  return a.d == 64 ? launch_d<64>(a) : launch_d<128>(a);
+}
+
+}  // namespace fa

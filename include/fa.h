@@ -1,0 +1,140 @@
+/*
+ * fa.h -- exact attention (FlashAttention forward) and paged-KV decode for AMD
+ * Instinct MI355X (gfx950), C ABI.
+ *
+ * What is computed (pages: "Phase 08 -- Inference Optimization at Depth",
+ * Concepts list and Lab 01; screna.ai interview notes, FlashAttention,
+ * online-softmax and MHA/MQA/GQA blocks):
+ *
+ *   S = scale * Q K^T,  causal: S[i][j] = -inf for j > i,
+ *   O = softmax(S) V,   L[i] = ln sum_j exp(S[i][j])   (natural log, fp32)
+ *
+ * computed tile by tile with the online-softmax recurrence (running row max and
+ * row sum, output accumulator rescaled per key tile), so the N x N score matrix
+ * is never stored: only O and L are written.  Query head h reads K/V head
+ * h / (Hq / Hkv) (grouped-query heads; Hkv == 1 is multi-query).
+ *
+ * Conventions shared by every entry point:
+ *   - All tensor pointers are DEVICE pointers to memory the caller allocated.
+ *     Tensors are dense, contiguous, row-major, with the layouts stated below,
+ *     and every tensor pointer must be 16-byte aligned.
+ *   - Inputs are read-only.  o and lse are fully overwritten and must not alias
+ *     any input.  The library never allocates, frees or synchronises.
+ *   - stream is a hipStream_t passed as void* (NULL = the default stream).  Work
+ *     is enqueued on it and the call returns; errors inside a running kernel are
+ *     not reported by the call.  Setting the environment variable FA_DEBUG=1
+ *     makes every call synchronise the stream and report kernel errors.
+ *   - Arguments are validated on the host before any HIP call; a failed check
+ *     returns its status code and launches nothing.
+ *   - A zero batch (B == 0, N == 0, or num_seqs == 0) is a no-op returning
+ *     FA_OK; pointers may then be NULL.
+ *   - Thread safety: the library has no mutable global state besides a
+ *     thread-local copy of the last HIP error text.
+ */
+#ifndef FA_MI355X_H
+#define FA_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define FA_OK              0 /* enqueued (or nothing to do)                        */
+#define FA_ERR_NULL        1 /* a required pointer is NULL                         */
+#define FA_ERR_SHAPE       2 /* negative size, Hq % Hkv != 0, Hq or Hkv < 1, ...   */
+#define FA_ERR_UNSUPPORTED 3 /* head dim not 64/128, page_size not 16             */
+#define FA_ERR_SCALE       4 /* scale is NaN or infinite                           */
+#define FA_ERR_ALIGN       5 /* a tensor pointer is not 16-byte aligned            */
+#define FA_ERR_WORKSPACE   6 /* decode workspace NULL or smaller than required     */
+#define FA_ERR_HIP         7 /* a HIP launch / runtime call failed                 */
+
+/*
+ * fa_fwd -- bf16 exact-attention forward (prefill).
+ *
+ * Pages: "Phase 08", Concepts (online softmax; FlashAttention tiling: Q in
+ * blocks of B_r rows, K/V streamed in blocks of B_c columns; only O and the
+ * logsumexp L stored; causal tiles that span the diagonal are handled apart
+ * from full and fully-masked ones) and Lab 01 steps 2 and 4 (tile Q, iterate
+ * K/V blocks, online softmax; skip future tiles entirely); getnybble
+ * "Inference Optimization -- Advanced", question 5 (parallelism over query
+ * blocks); screna.ai MHA/MQA/GQA block (grouped K/V heads).
+ *
+ *   q   [B, Hq,  N, d] bf16      k, v [B, Hkv, N, d] bf16
+ *   o   [B, Hq,  N, d] bf16 (out, fp32 accumulation, rounded to nearest even)
+ *   lse [B, Hq,  N]    fp32 (out, natural-log logsumexp of the scaled scores)
+ *   d in {64, 128}; Hq % Hkv == 0; N >= 0; causal: 0 or 1 (query i sees keys
+ *   j <= i); scale: any finite float (usually 1/sqrt(d)).
+ * Returns FA_OK or a status code above.
+ */
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+           int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+           void* stream);
+
+/*
+ * fa_fwd_f32 -- the same operation in fp32 throughout (inputs, the P V product
+ * with unrounded fp32 probabilities, accumulation and O).  Same pages, same
+ * parameter list and layouts as fa_fwd with every tensor fp32.
+ */
+int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
+               int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+               void* stream);
+
+/*
+ * fa_decode_paged_workspace_size -- bytes of device workspace fa_decode_paged
+ * needs for these sizes (fp32 split partials and their logsumexps).  Returns 0
+ * when an argument is out of range (negative size, unsupported d / page_size).
+ */
+size_t fa_decode_paged_workspace_size(int num_seqs, int Hq, int d,
+                                      int max_pages_per_seq, int page_size);
+
+/*
+ * fa_decode_paged -- one-query-per-sequence attention over a paged KV cache
+ * (decode), split along the context and merged with a log-sum-exp combine.
+ *
+ * Pages: "Phase 08", Concepts (KV cache; paged attention: the cache lives in
+ * non-contiguous fixed-size pages) and Lab 03 steps 1 and 4 (16-token pages; a
+ * kernel that reaches non-contiguous pages through an indirection table).
+ * Each split's partial result is combined with the online-softmax rescaling
+ * algebra of the Lab 01 talking points applied to whole splits.
+ *
+ *   q          [S, Hq, d] bf16          (S = num_seqs, one query per sequence)
+ *   kpages     [num_pages, Hkv, page_size, d] bf16   (one (page, head) block is
+ *   vpages     [num_pages, Hkv, page_size, d] bf16    page_size*d contiguous)
+ *   page_table [S, max_pages_per_seq] int32: logical page p of sequence s is
+ *              physical page page_table[s][p]; only entries p < ceil(ctx/page)
+ *              are read.
+ *   ctx_lens   [S] int32: tokens in each sequence's cache, 0 <= ctx_lens[s] <=
+ *              max_pages_per_seq * page_size.  Cache slots at or beyond
+ *              ctx_lens[s] are never allowed to affect the result, whatever they
+ *              hold (NaN included).  ctx_lens[s] == 0 gives O = 0, L = -inf.
+ *   o          [S, Hq, d] bf16 (out);  lse [S, Hq] fp32 (out, natural log).
+ *   d in {64, 128}; page_size == 16; Hq % Hkv == 0.
+ *   workspace: device memory of at least
+ *   fa_decode_paged_workspace_size(num_seqs, Hq, d, max_pages_per_seq,
+ *   page_size) bytes, owned by the caller, 16-byte aligned; its contents on
+ *   entry do not matter.  Two calls that share a workspace must be ordered
+ *   (same stream).
+ * Device-side values (ctx_lens, page ids) are trusted: out-of-range values give
+ * undefined output.  num_pages is used only by FA_DEBUG checks.
+ */
+int fa_decode_paged(const void* q, const void* kpages, const void* vpages,
+                    const int32_t* page_table, const int32_t* ctx_lens,
+                    void* o, float* lse,
+                    int num_seqs, int Hq, int Hkv, int d, int page_size,
+                    int max_pages_per_seq, int num_pages, float scale,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * fa_status_string -- static text for a status code.  For FA_ERR_HIP it is the
+ * text of the last HIP error seen by the calling thread.
+ */
+const char* fa_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_MI355X_H */

@@ -1,0 +1,106 @@
+"""The C-ABI library: it loads, exports every declared symbol, and rejects bad
+arguments on the host before touching the GPU (CPU only: no call here reaches a launch)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import exact_io_aware_15_amd as fa
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "fa.h")
+
+OK, NULL, SHAPE, UNSUP, SCALE, ALIGN, WORKSPACE, HIP = range(8)
+P = ctypes.c_void_p(0x10000)      # aligned stand-in device pointer, never dereferenced
+MIS = ctypes.c_void_p(0x10008)    # 8-byte aligned only
+Z = ctypes.c_void_p(0)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(fa.LIB_PATH):
+        pytest.fail("libfa.so is not built (python -m exact_io_aware_15_amd.build)")
+    return fa.lib()
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = declared_functions()
+    assert set(names) >= {"fa_fwd", "fa_fwd_f32", "fa_decode_paged", "fa_decode_paged_workspace_size",
+                          "fa_status_string"}
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_codes_match_header(L):
+    text = open(HEADER).read()
+    codes = dict((k, int(v)) for k, v in re.findall(r"#define (FA_\w+)\s+(\d+)", text))
+    assert codes == {"FA_OK": 0, "FA_ERR_NULL": 1, "FA_ERR_SHAPE": 2, "FA_ERR_UNSUPPORTED": 3,
+                     "FA_ERR_SCALE": 4, "FA_ERR_ALIGN": 5, "FA_ERR_WORKSPACE": 6, "FA_ERR_HIP": 7}
+    for c in range(8):
+        assert fa.fa_status_string(c)
+    assert fa.fa_status_string(99) == "unknown status"
+
+
+def fwd(L, entry, q=P, k=P, v=P, o=P, lse=P, B=1, Hq=2, Hkv=1, N=16, d=64, causal=0, scale=0.125):
+    return getattr(L, entry)(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, scale, Z)
+
+
+@pytest.mark.parametrize("entry", ["fa_fwd", "fa_fwd_f32"])
+def test_fwd_validation(L, entry):
+    assert fwd(L, entry, q=Z) == NULL
+    assert fwd(L, entry, lse=Z) == NULL
+    assert fwd(L, entry, d=96) == UNSUP
+    assert fwd(L, entry, d=256) == UNSUP
+    assert fwd(L, entry, Hq=3, Hkv=2) == SHAPE
+    assert fwd(L, entry, Hkv=0) == SHAPE
+    assert fwd(L, entry, N=-1) == SHAPE
+    assert fwd(L, entry, B=-2) == SHAPE
+    assert fwd(L, entry, causal=2) == SHAPE
+    assert fwd(L, entry, scale=float("nan")) == SCALE
+    assert fwd(L, entry, scale=float("inf")) == SCALE
+    assert fwd(L, entry, k=MIS) == ALIGN
+    assert fwd(L, entry, o=MIS) == ALIGN
+    # empty inputs are a no-op that needs no pointers
+    assert fwd(L, entry, q=Z, k=Z, v=Z, o=Z, lse=Z, B=0) == OK
+    assert fwd(L, entry, q=Z, k=Z, v=Z, o=Z, lse=Z, N=0) == OK
+
+
+def dec(L, q=P, kp=P, vp=P, pt=P, cl=P, o=P, lse=P, S=2, Hq=8, Hkv=2, d=128, ps=16, maxp=4, npages=9,
+        scale=0.1, ws=P, wsb=1 << 30):
+    return L.fa_decode_paged(q, kp, vp, pt, cl, o, lse, S, Hq, Hkv, d, ps, maxp, npages, scale, ws, wsb, Z)
+
+
+def test_decode_validation(L):
+    assert dec(L, q=Z) == NULL
+    assert dec(L, pt=Z) == NULL
+    assert dec(L, cl=Z) == NULL
+    assert dec(L, d=80) == UNSUP
+    assert dec(L, ps=32) == UNSUP
+    assert dec(L, Hq=6, Hkv=4) == SHAPE
+    assert dec(L, S=-1) == SHAPE
+    assert dec(L, maxp=0) == SHAPE
+    assert dec(L, scale=float("-inf")) == SCALE
+    assert dec(L, vp=MIS) == ALIGN
+    assert dec(L, ws=Z) == WORKSPACE
+    need = fa.fa_decode_paged_workspace_size(2, 8, 128, 4, 16)
+    assert dec(L, wsb=need - 1) == WORKSPACE
+    assert dec(L, ws=MIS, wsb=need) == ALIGN
+    assert dec(L, q=Z, kp=Z, vp=Z, pt=Z, cl=Z, o=Z, lse=Z, ws=Z, S=0) == OK
+
+
+def test_workspace_size(L):
+    # one fp32 partial (d values + one logsumexp) per (sequence, head, split of 32 pages)
+    for S, Hq, d, maxp in [(64, 32, 128, 1024), (1, 1, 64, 1), (3, 4, 64, 33)]:
+        splits = -(-maxp // 32)
+        o_bytes = S * Hq * splits * d * 4
+        assert fa.fa_decode_paged_workspace_size(S, Hq, d, maxp, 16) == -(-o_bytes // 256) * 256 + S * Hq * splits * 4
+    assert fa.fa_decode_paged_workspace_size(1, 1, 96, 1, 16) == 0
+    assert fa.fa_decode_paged_workspace_size(1, 1, 64, 1, 8) == 0
+    assert fa.fa_decode_paged_workspace_size(-1, 1, 64, 1, 16) == 0

@@ -1,0 +1,238 @@
+"""GPU parity: the HIP library against the fp64 oracle, element by element.
+
+Bars: fp32 O and L within 1e-4; bf16 O within 1e-2 and L within 1e-3 (max-abs over
+every compared element).  Small shapes compare every output element; the full-size
+workloads compare sampled query rows (every head and batch) that the oracle can
+evaluate one by one, plus the properties that hold at any size.  Outputs are
+pre-filled with NaN, so an element the kernels never write fails the check.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from exact_io_aware_15_amd import fa_decode_paged, fa_fwd, fa_fwd_f32
+from exact_io_aware_15_amd.workloads import CONFIGS, make_decode, make_inputs, make_prefill
+from oracle import attention_ref, decode_ref
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": (1e-4, 1e-4), "bf16": (1e-2, 1e-3)}
+DEV = "cuda:0"
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+def f64(t):
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def gpu_prefill(x, causal, dtype, scale=None):
+    q, k, v = (x[n].to(DEV) for n in "qkv")
+    fn = fa_fwd if dtype == "bf16" else fa_fwd_f32
+    out = torch.full(q.shape, float("nan"), dtype=q.dtype, device=DEV)
+    lse = torch.full(q.shape[:3], float("nan"), dtype=torch.float32, device=DEV)
+    fn(q, k, v, causal=causal, scale=scale, out=out, lse=lse)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+def check(O, L, Oref, Lref, dtype, what):
+    tol_o, tol_l = TOL[dtype]
+    assert np.all(np.isfinite(O)), f"{what}: non-finite O"
+    assert np.all(np.isfinite(L) | np.isneginf(Lref)), f"{what}: non-finite L"
+    eo = float(np.max(np.abs(O - Oref))) if O.size else 0.0
+    fin = np.isfinite(Lref)
+    el = float(np.max(np.abs(L[fin] - Lref[fin]))) if fin.any() else 0.0
+    floor = float(np.max(np.abs(f64(torch.from_numpy(Oref).to(torch.bfloat16)) - Oref))) if dtype == "bf16" and O.size else 0.0
+    say(f"{what}: max|dO|={eo:.3e} (bf16 output floor {floor:.3e}) max|dL|={el:.3e}")
+    assert eo <= tol_o, f"{what}: O error {eo} > {tol_o}"
+    assert el <= tol_l, f"{what}: L error {el} > {tol_l}"
+    assert np.all(np.isneginf(L[~fin])), f"{what}: empty rows must have L = -inf"
+
+
+SMALL = [
+    # B, Hq, Hkv, N, d, causal, dtype
+    (1, 1, 1, 1, 64, False, "bf16"),
+    (1, 1, 1, 2, 128, True, "bf16"),
+    (1, 2, 1, 3, 64, True, "bf16"),
+    (1, 1, 1, 17, 128, False, "bf16"),
+    (1, 2, 2, 65, 64, True, "bf16"),
+    (2, 4, 2, 127, 128, True, "bf16"),
+    (1, 4, 2, 600, 128, True, "bf16"),
+    (1, 4, 2, 600, 128, False, "bf16"),
+    (2, 2, 1, 333, 64, False, "bf16"),
+    (1, 2, 1, 513, 64, True, "bf16"),
+    (1, 8, 1, 300, 128, True, "bf16"),
+    (1, 1, 1, 1024, 128, True, "bf16"),
+    (1, 1, 1, 256, 64, False, "f32"),
+    (1, 2, 1, 130, 128, True, "f32"),
+    (2, 2, 2, 65, 64, True, "f32"),
+    (1, 1, 1, 1, 128, False, "f32"),
+    (1, 3, 1, 200, 64, False, "f32"),
+]
+
+
+@pytest.mark.parametrize("shape", SMALL, ids=lambda s: "B{}_Hq{}_Hkv{}_N{}_d{}_{}_{}".format(
+    s[0], s[1], s[2], s[3], s[4], "causal" if s[5] else "full", s[6]))
+def test_prefill_small_every_element(shape):
+    B, Hq, Hkv, N, d, causal, dtype = shape
+    say(f"prefill small {shape}")
+    x = make_prefill(B, Hq, Hkv, N, d, dtype, seed=100 + N + d)
+    out, lse = gpu_prefill(x, causal, dtype)
+    Oref, Lref = attention_ref(f64(x["q"]), f64(x["k"]), f64(x["v"]), causal, 1.0 / np.sqrt(d))
+    check(f64(out), f64(lse), Oref, Lref, dtype, str(shape))
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.0883883, 0.5])
+def test_prefill_scale_edge_cases(scale):
+    say(f"prefill scale {scale}")
+    x = make_prefill(1, 2, 1, 150, 128, "bf16", seed=7)
+    for causal in (False, True):
+        out, lse = gpu_prefill(x, causal, "bf16", scale=scale)
+        Oref, Lref = attention_ref(f64(x["q"]), f64(x["k"]), f64(x["v"]), causal, scale)
+        check(f64(out), f64(lse), Oref, Lref, "bf16", f"scale={scale} causal={causal}")
+
+
+def sample_rows(N, seed, extra=48):
+    rng = np.random.default_rng(seed)
+    fixed = [0, 1, 2, 3, 31, 32, 63, 64, 65, 127, 128, 255, 256, 257, 511, 512, N // 2, N - 2, N - 1]
+    rows = set(r for r in fixed if 0 <= r < N) | set(rng.choice(N, size=min(extra, N), replace=False).tolist())
+    return np.array(sorted(rows))
+
+
+PREFILL_CFGS = [n for n, c in CONFIGS.items() if c.kind == "prefill"]
+
+
+@pytest.mark.parametrize("name", PREFILL_CFGS)
+def test_prefill_full_size_sampled_rows(name):
+    cfg = CONFIGS[name]
+    say(f"full-size prefill {name}")
+    x = make_inputs(cfg)
+    out, lse = gpu_prefill(x, cfg.causal, cfg.dtype)
+    rows = np.arange(cfg.N) if cfg.N <= 256 else sample_rows(cfg.N, cfg.seed)
+    Oref, Lref = attention_ref(f64(x["q"]), f64(x["k"]), f64(x["v"]), cfg.causal, cfg.scale, rows=rows)
+    O = f64(out[:, :, torch.from_numpy(rows).to(DEV)])
+    L = f64(lse[:, :, torch.from_numpy(rows).to(DEV)])
+    check(O, L, Oref, Lref, cfg.dtype, f"{name} ({len(rows)} rows x {cfg.B * cfg.Hq} heads)")
+    # every element written and finite, at every row
+    assert torch.isfinite(out).all().item() and torch.isfinite(lse).all().item()
+
+
+def test_prefill_gqa_equals_mha_on_repeated_kv_bitwise():
+    say("gqa vs repeated-kv mha")
+    x = make_prefill(2, 8, 2, 400, 128, "bf16", seed=11)
+    o1, l1 = gpu_prefill(x, True, "bf16")
+    xr = {"q": x["q"], "k": x["k"].repeat_interleave(4, dim=1).contiguous(),
+          "v": x["v"].repeat_interleave(4, dim=1).contiguous()}
+    o2, l2 = gpu_prefill(xr, True, "bf16")
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_prefill_deterministic():
+    say("prefill determinism")
+    x = make_prefill(1, 4, 4, 700, 64, "bf16", seed=12)
+    a = gpu_prefill(x, True, "bf16")
+    b = gpu_prefill(x, True, "bf16")
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+# ------------------------------------------------------------------------------ decode
+
+def gpu_decode(x, scale=None):
+    dev = {k: (v.to(DEV) if torch.is_tensor(v) else v) for k, v in x.items()}
+    S, Hq, d = x["q"].shape
+    out = torch.full((S, Hq, d), float("nan"), dtype=torch.bfloat16, device=DEV)
+    lse = torch.full((S, Hq), float("nan"), dtype=torch.float32, device=DEV)
+    fa_decode_paged(dev["q"], dev["kpages"], dev["vpages"], dev["page_table"], dev["ctx_lens"],
+                    scale=scale, out=out, lse=lse)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+def oracle_decode(x, scale):
+    return decode_ref(f64(x["q"]), x["kpages"].float().numpy(), x["vpages"].float().numpy(),
+                      x["page_table"].numpy(), x["ctx_lens"].numpy(), scale)
+
+
+DECODE_SMALL = [
+    # S, Hq, Hkv, d, ctx lens
+    (6, 4, 4, 128, (1, 15, 16, 17, 100, 513)),
+    (5, 8, 2, 64, (0, 1, 511, 512, 1000)),
+    (4, 32, 8, 128, (2048, 3, 16 * 32 + 1, 777)),
+    (3, 16, 2, 128, (5, 70, 1600)),   # 8 query heads per K/V head
+    (3, 8, 1, 64, (33, 1, 64)),       # multi-query
+    (2, 2, 1, 128, (16384, 9999)),
+]
+
+
+@pytest.mark.parametrize("case", DECODE_SMALL, ids=lambda c: f"S{c[0]}_Hq{c[1]}_Hkv{c[2]}_d{c[3]}")
+def test_decode_small_every_element(case):
+    S, Hq, Hkv, d, lens = case
+    say(f"decode {case}")
+    x = make_decode(S, Hq, Hkv, d, seed=200 + S, fixed_ctx=lens)
+    out, lse = gpu_decode(x)
+    Oref, Lref = oracle_decode(x, 1.0 / np.sqrt(d))
+    check(f64(out), f64(lse), Oref, Lref, "bf16", str(case))
+    for s, n in enumerate(lens):
+        if n == 0:
+            assert torch.all(out[s] == 0).item() and torch.all(torch.isneginf(lse[s])).item()
+
+
+def test_decode_full_size_every_element():
+    cfg = CONFIGS["c5_bf16_paged_decode_S64_Hq32_Hkv8_d128"]
+    say("decode full size c5")
+    x = make_inputs(cfg)
+    out, lse = gpu_decode(x)
+    Oref, Lref = oracle_decode(x, cfg.scale)
+    check(f64(out), f64(lse), Oref, Lref, "bf16", cfg.name)
+
+
+def test_decode_page_permutation_is_bitwise_invariant():
+    say("decode page permutation")
+    x = make_decode(4, 8, 2, 128, seed=31, fixed_ctx=(700, 17, 1500, 64))
+    a = gpu_decode(x)
+    # move every used page to a new physical slot and rewrite the table accordingly
+    P = x["num_pages"]
+    perm = torch.from_numpy(np.random.default_rng(5).permutation(P - 1)).long()
+    new_k = x["kpages"].clone()
+    new_v = x["vpages"].clone()
+    new_k[perm] = x["kpages"][: P - 1]
+    new_v[perm] = x["vpages"][: P - 1]
+    table = x["page_table"].clone().long()
+    used = table < P - 1
+    table[used] = perm[table[used]]
+    y = dict(x, kpages=new_k, vpages=new_v, page_table=table.to(torch.int32))
+    b = gpu_decode(y)
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+def test_decode_matches_last_row_of_causal_prefill():
+    say("decode vs causal prefill")
+    Hq, Hkv, n, d = 8, 2, 777, 128
+    x = make_prefill(1, Hq, Hkv, n, d, "bf16", seed=41)
+    o_pf, l_pf = gpu_prefill(x, True, "bf16")
+    # page the contiguous K/V of the one sequence, in order, 16 tokens per page
+    npg = -(-n // 16)
+    kp = torch.zeros((npg + 1, Hkv, 16, d), dtype=torch.bfloat16)
+    vp = torch.zeros_like(kp)
+    for p in range(npg):
+        t1 = min(n, (p + 1) * 16)
+        kp[p, :, : t1 - p * 16] = x["k"][0, :, p * 16:t1]
+        vp[p, :, : t1 - p * 16] = x["v"][0, :, p * 16:t1]
+    y = {"q": x["q"][0, :, n - 1].contiguous().unsqueeze(0), "kpages": kp, "vpages": vp,
+         "page_table": torch.arange(npg, dtype=torch.int32).unsqueeze(0),
+         "ctx_lens": torch.tensor([n], dtype=torch.int32)}
+    o_dc, l_dc = gpu_decode(y)
+    assert float((o_dc[0].float() - o_pf[0, :, n - 1].float()).abs().max()) <= 1e-2
+    assert float((l_dc[0] - l_pf[0, :, n - 1]).abs().max()) <= 1e-3
+
+
+def test_decode_deterministic():
+    say("decode determinism")
+    x = make_decode(3, 8, 2, 128, seed=51, fixed_ctx=(3000, 10, 900))
+    a = gpu_decode(x)
+    b = gpu_decode(x)
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
