@@ -1,0 +1,261 @@
+#!/usr/bin/env python3
+"""Benchmark: one step = the whole hot path once -- a causal bf16 FlashAttention
+forward (B1 Hq32 N8192 d128, inputs 0.5*N(0,1)) followed by a paged bf16 decode
+(64 sequences, Hq32 Hkv8 d128, context U[1024,16384], 16-token pages).
+
+Prints ONE JSON line.  `value` is the forward's throughput in TFLOP/s (causal FLOPs
+counted as half: 2*B*Hq*N^2*d) from HIP events around its launches; the decode's
+GB/s (algorithmic bytes: every valid K/V token once, plus q, O, L, the used page
+table entries and ctx_lens) is reported beside it.  Both carry a roofline object
+against the MI355X peaks (bf16 dense MFMA 2516.6 TFLOP/s = 256 CU x 2.4 GHz x 4096
+flop/clk; HBM3E 8000 GB/s).  `cpu_baseline` times the fp64 CPU oracle on a bounded
+sample of the same workload.
+
+Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--no-cpu-baseline]
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "attention fwd TFLOP/s + % bf16 MFMA peak; paged decode GB/s + % HBM peak"
+PEAK_BF16_TFLOPS = 2516.6
+PEAK_HBM_GBS = 8000.0
+PREFILL = "c3_bf16_causal_B1_H32_N8192_d128"
+DECODE = "c5_bf16_paged_decode_S64_Hq32_Hkv8_d128"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def source_digest(files):
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, "exact_io_aware_15_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+KERNEL_SOURCES = {
+    "prefill": ["fa_device.h", "fa_launch.h", "fa_prefill_bf16.hip"],
+    "decode": ["fa_device.h", "fa_launch.h", "fa_decode.hip"],
+}
+
+
+def measured_traffic(kind):
+    """HBM bytes per launch from the committed rocprofv3 counter runs, or None when the
+    kernel sources changed since those counters were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)[kind]
+    except (OSError, KeyError, ValueError):
+        return None
+    if t.get("source_digest") != source_digest(KERNEL_SOURCES[kind]):
+        return None
+    return t.get("bytes_per_launch")
+
+
+def prefill_flops(cfg):
+    f = 4.0 * cfg.B * cfg.Hq * cfg.N * cfg.N * cfg.d
+    return f / 2 if cfg.causal else f
+
+
+def decode_bytes(x, cfg):
+    ctx = x["ctx_lens"].long()
+    kv = int(ctx.sum()) * cfg.Hkv * cfg.d * 2 * 2
+    qo = 2 * cfg.num_seqs * cfg.Hq * cfg.d * 2
+    lse = cfg.num_seqs * cfg.Hq * 4
+    pages_used = int(((ctx + cfg.page_size - 1) // cfg.page_size).sum())
+    return kv + qo + lse + pages_used * 4 + cfg.num_seqs * 4
+
+
+def cpu_baseline_prefill(x, cfg, stride):
+    """fp64 oracle on every `stride`-th query row of every head (bounded sample)."""
+    import numpy as np
+    import threadpoolctl
+
+    from oracle import attention_ref
+
+    q, k, v = (x[n].float().numpy() for n in "qkv")
+    rows = np.arange(0, cfg.N, stride)
+    t0 = time.perf_counter()
+    attention_ref(q, k, v, cfg.causal, cfg.scale, rows=rows)
+    dt = time.perf_counter() - t0
+    vis = (rows + 1) if cfg.causal else np.full(rows.shape, cfg.N)
+    flops = 4.0 * cfg.d * float(vis.sum()) * cfg.B * cfg.Hq
+    threads = max(i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()) or 1
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"every {stride}th query row ({len(rows)} rows) of all {cfg.B * cfg.Hq} heads of {cfg.name}; "
+                      f"{dt:.1f} s of fp64 numpy",
+            "seconds": round(dt, 2)}
+
+
+def cpu_baseline_decode(x, cfg, nseq):
+    import numpy as np
+    import threadpoolctl
+
+    from oracle import decode_ref
+
+    kp = x["kpages"].float().numpy()  # bf16 -> fp32 view for numpy, outside the timed region
+    vp = x["vpages"].float().numpy()
+    sub = slice(0, nseq)
+    qs = x["q"][sub].float().numpy()
+    t0 = time.perf_counter()
+    decode_ref(qs, kp, vp, x["page_table"][sub].numpy(), x["ctx_lens"][sub].numpy(), cfg.scale)
+    dt = time.perf_counter() - t0
+    ctx = x["ctx_lens"][sub].long()
+    byts = int(ctx.sum()) * cfg.Hkv * cfg.d * 4 + 2 * nseq * cfg.Hq * cfg.d * 2
+    threads = max(i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()) or 1
+    return {"value": byts / dt / 1e9, "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{nseq} of {cfg.num_seqs} sequences of {cfg.name} (all heads, every valid token); "
+                      f"{dt:.1f} s of fp64 numpy incl. the page gather",
+            "seconds": round(dt, 2)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-row-stride", type=int, default=4)
+    ap.add_argument("--only", choices=["prefill", "decode"], default=None,
+                    help="time one half of the step only (for profiling runs)")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB 5 times (calibrates the "
+                         "FETCH_SIZE / WRITE_SIZE counters against a known byte count) and exit")
+    args = ap.parse_args()
+    if args.copy_probe:
+        import torch
+
+        n = args.copy_probe * (1 << 20)
+        src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": n, "launches": 5}), flush=True)
+        return
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: this build runs on a single MI355X and has no multi-GPU "
+              "path (run with --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import exact_io_aware_15_amd as fa
+    from exact_io_aware_15_amd.workloads import CONFIGS, make_inputs
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    pcfg, dcfg = CONFIGS[PREFILL], CONFIGS[DECODE]
+    run_p = args.only in (None, "prefill")
+    run_d = args.only in (None, "decode")
+
+    log("generating inputs")
+    px = make_inputs(pcfg) if run_p else None
+    dx = make_inputs(dcfg) if run_d else None
+    if run_p:
+        q, k, v = (px[n].to(dev) for n in "qkv")
+        o = torch.empty_like(q)
+        lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+    if run_d:
+        dq, kp, vp = dx["q"].to(dev), dx["kpages"].to(dev), dx["vpages"].to(dev)
+        pt, cl = dx["page_table"].to(dev), dx["ctx_lens"].to(dev)
+        do = torch.empty_like(dq)
+        dl = torch.empty(dq.shape[:2], dtype=torch.float32, device=dev)
+        ws = torch.empty(fa.fa_decode_paged_workspace_size(dcfg.num_seqs, dcfg.Hq, dcfg.d,
+                                                           dx["max_pages_per_seq"]), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+
+    def prefill():
+        fa.fa_fwd(q, k, v, causal=pcfg.causal, scale=pcfg.scale, out=o, lse=lse)
+
+    def decode():
+        fa.fa_decode_paged(dq, kp, vp, pt, cl, scale=dcfg.scale, out=do, lse=dl, workspace=ws)
+
+    log(f"warmup {args.warmup}")
+    for _ in range(args.warmup):
+        if run_p:
+            prefill()
+        if run_d:
+            decode()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    log(f"timing {K} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        ev[i][0].record()
+        if run_p:
+            prefill()
+        ev[i][1].record()
+        if run_d:
+            decode()
+        ev[i][2].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    p_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / K
+    d_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / K
+    step_ms = ev[0][0].elapsed_time(ev[-1][2]) / K
+    log(f"prefill {p_ms:.4f} ms, decode {d_ms:.4f} ms, step {step_ms:.4f} ms (wall {wall * 1e3 / K:.4f} ms)")
+
+    res = {"metric": METRIC, "n_gpus": 1, "steps": K, "warmup": args.warmup, "ms_per_step": round(step_ms, 5),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+           "data": "synthetic (seeded N(0,1) inputs; random page permutation)"}
+    cfg_desc = {"workload": "one step = causal bf16 prefill B1 Hq32 Hkv32 N8192 d128 (inputs 0.5*N(0,1)) "
+                            "+ paged bf16 decode 64 seqs Hq32 Hkv8 d128 ctx~U[1024,16384] 16-token pages"}
+    if run_p:
+        fl = prefill_flops(pcfg)
+        tf = fl / (p_ms * 1e-3) / 1e12
+        tr = measured_traffic("prefill")
+        res.update({"value": round(tf, 2), "unit": "TFLOP/s"})
+        res["roofline"] = {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                           "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": tr,
+                           "kernel": "fwd_bf16_kernel<128, causal>", "ms": round(p_ms, 5),
+                           "algorithmic_flops_per_launch": fl}
+        cfg_desc["prefill"] = {"B": pcfg.B, "Hq": pcfg.Hq, "Hkv": pcfg.Hkv, "N": pcfg.N, "d": pcfg.d,
+                               "causal": pcfg.causal, "seed": pcfg.seed}
+    if run_d:
+        by = decode_bytes(dx, dcfg)
+        gbs = by / (d_ms * 1e-3) / 1e9
+        dec = {"value": round(gbs, 1), "unit": "GB/s", "ms": round(d_ms, 5),
+               "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                            "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": measured_traffic("decode"),
+                            "kernel": "decode_split_kernel<128, 4> + decode_merge_kernel<128>",
+                            "algorithmic_bytes_per_launch": by}}
+        res["decode"] = dec
+        cfg_desc["decode"] = {"num_seqs": dcfg.num_seqs, "Hq": dcfg.Hq, "Hkv": dcfg.Hkv, "d": dcfg.d,
+                              "page_size": dcfg.page_size, "ctx_total": int(dx["ctx_lens"].long().sum()),
+                              "seed": dcfg.seed}
+        if not run_p:
+            res.update({"value": dec["value"], "unit": "GB/s", "roofline": dec["roofline"]})
+    res["config"] = cfg_desc
+    if not args.no_cpu_baseline:
+        log("timing the fp64 CPU oracle on a bounded sample")
+        if run_p:
+            res["cpu_baseline"] = cpu_baseline_prefill(px, pcfg, args.cpu_row_stride)
+        if run_d:
+            cb = cpu_baseline_decode(dx, dcfg, 32)
+            if run_p:
+                res["decode"]["cpu_baseline"] = cb
+            else:
+                res["cpu_baseline"] = cb
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()
