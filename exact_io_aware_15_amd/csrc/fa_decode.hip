@@ -6,11 +6,12 @@
 // Phase 1 (decode_split_kernel): one workgroup per (split of 32 pages, K/V head,
 // sequence) serves up to HB query heads of that K/V head's group, so each K/V
 // page is read from HBM once for the whole group.  Its 4 waves take the split's
-// pages round-robin.  In a wave, lane l holds tokens 2*(l/8) and 2*(l/8)+1 of
-// the page and the d columns {8*(l%8) + 64*c .. +8}; each (page, head) block is
-// 4 KB contiguous, so every 16-byte load instruction covers 8 whole 128-byte
-// row segments.  The next page is fetched while the current one is consumed.
-// Scores: per-lane FMAs then a 3-step DPP sum over the 8 lanes of a token.  The
+// pages two at a time, round-robin.  In a wave, lane l holds tokens 2*(l/8) and
+// 2*(l/8)+1 of each page and the d columns {8*(l%8) + 64*c .. +8}; each (page,
+// head) block is 4 KB contiguous, so every 16-byte load instruction covers 8
+// whole 128-byte row segments.  The next page pair is fetched while the current
+// one is consumed.  Scores: bf16 pair dot products (v_dot2c_f32_bf16, fp32
+// accumulation) then a 3-step DPP sum over the 8 lanes of a token.  The
 // wave keeps the online-softmax state (running max m, sum l, unnormalised
 // accumulator) of the "Phase 08" Lab 01 recurrence, rescaling only when a head's
 // max grows.  Tokens at or past ctx_len get probability 0 and their V rows are
@@ -38,6 +39,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
     float* __restrict__ ws_l, int Hq, int Hkv, int max_pages, int max_splits, int nhb, float c) {
   constexpr int CPL = D / 64;  // 8-column chunks per token per lane
   constexpr int DL = CPL * 8;  // d columns per lane
+  constexpr int PP = 2;        // pages consumed per wave iteration
   __shared__ float sm_m[kDecWaves][HB];
   __shared__ float sm_l[kDecWaves][HB];
   __shared__ float sm_acc[kDecWaves][HB][D];
@@ -59,22 +61,22 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
   const int tg = lane >> 3;  // token pair within the page
   const int dg = lane & 7;   // column group
 
-  // query heads served: h = g*G + hb*HB + hh, valid while hb*HB + hh < G
-  float qv[HB][DL];
+  // query heads served: h = g*G + hb*HB + hh, valid while hb*HB + hh < G.
+  // q stays packed bf16 (two columns per register) for the dot2 score products.
+  uint32_t qp[HB][DL / 2];
+  float qscale[HB];
 #pragma unroll
   for (int hh = 0; hh < HB; ++hh) {
     const int hl = hb * HB + hh;
     const bool ok = hl < G;
-    const uint16_t* qp = Q + ((size_t)s * Hq + g * G + (ok ? hl : 0)) * D;
+    const uint16_t* qrow = Q + ((size_t)s * Hq + g * G + (ok ? hl : 0)) * D;
 #pragma unroll
     for (int cc = 0; cc < CPL; ++cc) {
-      u32x4 x = ldg16(qp + (dg + 8 * cc) * 8);
+      const u32x4 x = ldg16(qrow + (dg + 8 * cc) * 8);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        qv[hh][cc * 8 + 2 * e] = ok ? bf16lo_to_f32(x[e]) * c : 0.f;
-        qv[hh][cc * 8 + 2 * e + 1] = ok ? bf16hi_to_f32(x[e]) * c : 0.f;
-      }
+      for (int e = 0; e < 4; ++e) qp[hh][cc * 4 + e] = ok ? x[e] : 0u;
     }
+    qscale[hh] = c;
   }
 
   float m_run[HB], l_run[HB], acc[HB][DL];
@@ -90,52 +92,62 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
   const size_t head_off = (size_t)g * kPage * D;
   const size_t page_stride = (size_t)Hkv * kPage * D;
 
-  u32x4 kc[2][CPL], vc[2][CPL];  // current page
-  u32x4 kn[2][CPL], vn[2][CPL];  // next page
-  auto fetch = [&](int p, u32x4 (&kd)[2][CPL], u32x4 (&vd)[2][CPL]) {
-    const size_t base = (size_t)trow[p] * page_stride + head_off;
+  // register buffers: [page of the pair][token of the lane][chunk]
+  u32x4 kc[PP][2][CPL], vc[PP][2][CPL];
+  u32x4 kn[PP][2][CPL], vn[PP][2][CPL];
+  auto fetch = [&](int p0, u32x4 (&kd)[PP][2][CPL], u32x4 (&vd)[PP][2][CPL]) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int pp = 0; pp < PP; ++pp) {
+      const int p = p0 + pp;
+      const bool have = p < p_end;
+      const size_t base = (size_t)trow[have ? p : p0] * page_stride + head_off;
 #pragma unroll
-      for (int cc = 0; cc < CPL; ++cc) {
-        const size_t off = base + (size_t)(2 * tg + j) * D + (dg + 8 * cc) * 8;
-        kd[j][cc] = ldg16(KPg + off);
-        vd[j][cc] = ldg16(VPg + off);
-      }
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int cc = 0; cc < CPL; ++cc) {
+          const size_t off = base + (size_t)(2 * tg + j) * D + (dg + 8 * cc) * 8;
+          const u32x4 z = {0u, 0u, 0u, 0u};
+          kd[pp][j][cc] = have ? ldg16(KPg + off) : z;
+          vd[pp][j][cc] = have ? ldg16(VPg + off) : z;
+        }
+    }
   };
 
-  int p = p_begin + w;
+  // wave w takes page pairs (p_begin + PP*w, +1), (p_begin + PP*(w + 4), +1), ...
+  int p = p_begin + PP * w;
   if (p < p_end) fetch(p, kc, vc);
-  for (; p < p_end; p += kDecWaves) {
-    const int pn = p + kDecWaves;
+  for (; p < p_end; p += PP * kDecWaves) {
+    const int pn = p + PP * kDecWaves;
     if (pn < p_end) fetch(pn, kn, vn);
 
-    // scores for this lane's two tokens, every served head
-    float sc[2][HB];
+    // scores: this lane's 2 tokens of each page of the pair, every served head
+    float sc[PP][2][HB];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int tok = p * kPage + 2 * tg + j;
-      const bool valid = tok < n;
+    for (int pp = 0; pp < PP; ++pp)
 #pragma unroll
-      for (int hh = 0; hh < HB; ++hh) {
-        float part = 0.f;
+      for (int j = 0; j < 2; ++j) {
+        const int tok = (p + pp) * kPage + 2 * tg + j;
+        const bool valid = tok < n;
 #pragma unroll
-        for (int cc = 0; cc < CPL; ++cc)
+        for (int hh = 0; hh < HB; ++hh) {
+          float part = 0.f;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            part = __builtin_fmaf(qv[hh][cc * 8 + 2 * e], bf16lo_to_f32(kc[j][cc][e]), part);
-            part = __builtin_fmaf(qv[hh][cc * 8 + 2 * e + 1], bf16hi_to_f32(kc[j][cc][e]), part);
-          }
-        part = sum8(part);
-        sc[j][hh] = valid ? part : -INFINITY;
+          for (int cc = 0; cc < CPL; ++cc)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              part = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(kc[pp][j][cc][e]), as_bf16x2(qp[hh][cc * 4 + e]),
+                                                     part, false);
+          part = sum8(part) * qscale[hh];
+          sc[pp][j][hh] = valid ? part : -INFINITY;
+        }
       }
-    }
     // online softmax state update (wave-uniform max per head)
     bool grow = false;
     float mnew[HB];
 #pragma unroll
     for (int hh = 0; hh < HB; ++hh) {
-      const float pm = max_stride8(fmaxf(sc[0][hh], sc[1][hh]));
+      float pm = fmaxf(fmaxf(sc[0][0][hh], sc[0][1][hh]), fmaxf(sc[1][0][hh], sc[1][1][hh]));
+      pm = max_stride8(pm);
       mnew[hh] = fmaxf(m_run[hh], pm);
       grow |= mnew[hh] > m_run[hh];
     }
@@ -149,39 +161,47 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
         m_run[hh] = mnew[hh];
       }
     }
-    // the last page may hold slots past ctx_len: zero their V so 0 * NaN cannot occur
-    if ((p + 1) * kPage > n) {
+    // the sequence's last page may hold slots past ctx_len: zero their V so that
+    // 0 * NaN cannot occur
+    if ((p + PP) * kPage > n) {
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const bool valid = p * kPage + 2 * tg + j < n;
+      for (int pp = 0; pp < PP; ++pp)
 #pragma unroll
-        for (int cc = 0; cc < CPL; ++cc)
+        for (int j = 0; j < 2; ++j) {
+          const bool valid = (p + pp) * kPage + 2 * tg + j < n;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) vc[j][cc][e] = valid ? vc[j][cc][e] : 0u;
-      }
+          for (int cc = 0; cc < CPL; ++cc)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) vc[pp][j][cc][e] = valid ? vc[pp][j][cc][e] : 0u;
+        }
     }
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int pp = 0; pp < PP; ++pp)
 #pragma unroll
-      for (int hh = 0; hh < HB; ++hh) {
-        const float pr = (sc[j][hh] == -INFINITY) ? 0.f : exp2_fast(sc[j][hh] - m_run[hh]);
-        l_run[hh] += pr;
+      for (int j = 0; j < 2; ++j)
 #pragma unroll
-        for (int cc = 0; cc < CPL; ++cc)
+        for (int hh = 0; hh < HB; ++hh) {
+          const float pr = (sc[pp][j][hh] == -INFINITY) ? 0.f : exp2_fast(sc[pp][j][hh] - m_run[hh]);
+          l_run[hh] += pr;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            acc[hh][cc * 8 + 2 * e] = __builtin_fmaf(pr, bf16lo_to_f32(vc[j][cc][e]), acc[hh][cc * 8 + 2 * e]);
-            acc[hh][cc * 8 + 2 * e + 1] =
-                __builtin_fmaf(pr, bf16hi_to_f32(vc[j][cc][e]), acc[hh][cc * 8 + 2 * e + 1]);
-          }
-      }
+          for (int cc = 0; cc < CPL; ++cc)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+            for (int e = 0; e < 4; ++e) {
+              acc[hh][cc * 8 + 2 * e] =
+                  __builtin_fmaf(pr, bf16lo_to_f32(vc[pp][j][cc][e]), acc[hh][cc * 8 + 2 * e]);
+              acc[hh][cc * 8 + 2 * e + 1] =
+                  __builtin_fmaf(pr, bf16hi_to_f32(vc[pp][j][cc][e]), acc[hh][cc * 8 + 2 * e + 1]);
+            }
+        }
 #pragma unroll
-      for (int cc = 0; cc < CPL; ++cc) {
-        kc[j][cc] = kn[j][cc];
-        vc[j][cc] = vn[j][cc];
-      }
+    for (int pp = 0; pp < PP; ++pp)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int cc = 0; cc < CPL; ++cc) {
+          kc[pp][j][cc] = kn[pp][j][cc];
+          vc[pp][j][cc] = vn[pp][j][cc];
+        }
   }
 
   // combine the 8 token-pair lanes of each column group, then the 4 waves

@@ -31,9 +31,18 @@ __device__ __forceinline__ float bf16hi_to_f32(uint32_t w) { return __uint_as_fl
 // fp32 -> bf16, round to nearest even (gfx950 converts in hardware).
 __device__ __forceinline__ __bf16 to_bf16(float x) { return (__bf16)x; }
 
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Reinterpret one 32-bit word as two bf16.  Takes the word by value: a bit cast
+// applied directly to an element of a vector register is lowered as a cast of
+// element 0, so vector elements must be copied out first.
+__device__ __forceinline__ bf16x2 as_bf16x2(uint32_t w) { return __builtin_bit_cast(bf16x2, w); }
+
+// Two fp32 -> two bf16 (RNE) in one v_cvt_pk_bf16_f32; a in the low half.
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  __bf16 lo = to_bf16(a), hi = to_bf16(b);
-  return (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+  const f32x2 v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
 // ---- DPP / permlane cross-lane moves ------------------------------------------
