@@ -6,14 +6,14 @@
 // "Inference Optimization -- Advanced", question 5, and the grouped K/V heads of
 // the screna.ai MHA/MQA/GQA block.
 //
-// Work decomposition: one workgroup of 4 waves (one per SIMD) per (256-row query
-// block, query head, batch).  Each wave owns 64 query rows as two 32-row MFMA
-// blocks and keeps their Q fragments in registers for the whole pass.  K/V are
-// streamed in tiles of 64 keys through two LDS buffers: the next tile is copied
-// HBM -> LDS by 128-bit buffer loads with the LDS-destination bit (no staging
-// registers; rows past N read as zero) while the current one is consumed.  Rows
-// are stored unpadded with their 16-byte chunks XOR-swizzled by row, so both the
-// b128 K reads and the transposing V reads hit distinct LDS banks.  Per tile and wave:
+// Work decomposition: one workgroup of 8 waves (two per SIMD) per (256-row query
+// block, query head, batch).  Each wave owns 32 query rows and keeps their Q
+// fragments in registers for the whole pass.  K/V are streamed in tiles of 64
+// keys through two LDS buffers: the next tile is copied HBM -> LDS by 128-bit
+// buffer loads with the LDS-destination bit (no staging registers; rows past N
+// read as zero) while the current one is consumed.  Rows are stored unpadded
+// with their 16-byte chunks XOR-swizzled by row, so the b128 K reads and the
+// transposing V reads both hit distinct LDS banks.  Per tile and wave:
 //   S^T = K Q^T  with v_mfma_f32_32x32x16_bf16 (K from LDS is the A operand, so
 //                every lane ends up holding 16 keys of one query row),
 //   online softmax in the log2 domain (row max over the lane's keys plus one
@@ -22,16 +22,18 @@
 //                row-major LDS tile through ds_read_b64_tr_b16, and P stays in
 //                the registers the S MFMA produced (the key order inside a
 //                16-key step is permuted identically on both operands).
-// The two row blocks are software-pipelined inside the wave: the S MFMAs of block
-// 1 are issued next to the softmax arithmetic of block 0, and the PV MFMAs of
-// block 0 next to the softmax of block 1, so the matrix cores and the vector ALU
-// work at the same time.
+// The two waves sharing a SIMD interleave one's exponentials with the other's
+// matrix instructions.
 //
-// Rescaling follows the running-max recurrence exactly: a row's m rises to its
-// tile max whenever that is larger, and O and l are multiplied by exp(m_old -
-// m_new).  The multiply is skipped, wave-wide, on tiles where no row's max grew
-// (then every factor would be 1).  The largest score of a tile that sets m gets
-// probability exactly 1, which keeps the bf16 rounding of P off the dominant key.
+// Rescaling (the running-max recurrence): the max m used in the exponentials is
+// raised only when a row's tile max exceeds it by more than kRescaleThreshold
+// (log2 units), and then O and the sums are multiplied by exp2(m_old - m_new);
+// otherwise the previous m is kept, so probabilities stay below 2^threshold and
+// the vector-ALU rescale of O is skipped.  The same m is used for O, l and L,
+// so this computes the same exact attention.  O is normalised by the sum of the
+// bf16-rounded probabilities that actually entered the P V product (one bf16
+// dot2 per pair), so O is a weighted mean with consistent weights; L uses the
+// fp32 sum of the unrounded probabilities.
 //
 // Causal: tiles wholly above a wave's rows are skipped, tiles crossing the
 // diagonal (or the ragged end of the sequence) take the masked path, every other
@@ -43,12 +45,12 @@
 namespace fa {
 namespace {
 
-constexpr int kRB = 1;                      // 32-row MFMA blocks per wave
-constexpr int kRowsPerWave = 32 * kRB;
+constexpr int kRowsPerWave = 32;            // one 32-row MFMA block per wave
 constexpr int kWaves = 8;                   // two waves per SIMD
 constexpr int kThreads = kWaves * 64;
 constexpr int kBR = kWaves * kRowsPerWave;  // 256 query rows per workgroup
 constexpr int kBC = 64;                     // keys per tile (two 32-key MFMA blocks)
+constexpr float kRescaleThreshold = 8.0f;   // log2 units: probabilities stay <= 256
 
 template <int D>
 struct Lay {
@@ -59,9 +61,15 @@ struct Lay {
   static constexpr int BUF = 2 * TBYTES;        // K tile then V tile
   static constexpr int BLOCKS = TBYTES / 1024;  // 1 KB copies per tensor tile
   static constexpr int BPW = BLOCKS / kWaves;   // ... per wave
-  // chunk swizzles: physical chunk = logical chunk ^ swz(row)
-  __device__ static constexpr int swz_k(int r) { return r & (CPR - 1); }
-  __device__ static constexpr int swz_v(int r) { return (r & (CPR / 2 - 1)) << 1; }
+  static_assert(BPW * kWaves == BLOCKS, "tile copy must split evenly over the waves");
+  // Chunk swizzles (physical chunk = logical chunk ^ swz(row)).
+  // K: the 16 rows read together by a b128 instruction land on 16 distinct
+  //    16-byte bank groups.
+  __host__ __device__ static constexpr int swz_k(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
+  // V: each 16-lane group of a transposing read touches 4 rows x 32 bytes; the
+  //    swizzle moves whole 32-byte pairs so the 8 (row, pair) accesses of a
+  //    32-lane half are bank-disjoint.
+  __host__ __device__ static constexpr int swz_v(int r) { return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
 };
 
 __device__ __forceinline__ u32x4 ld_global16(const void* p) {
@@ -75,157 +83,156 @@ template <int D>
 struct WaveState {
   static constexpr int KK = D / 16;
   static constexpr int DB = D / 32;
-  bf16x8 qf[kRB][KK];     // Q^T fragments (B operand), one per 32-row block
-  f32x16 oacc[kRB][DB];   // O^T accumulators: lane holds row l%32, 16 d values per block
-  float m_run[kRB];       // max used in the exponentials (log2 units)
-  float l_run[kRB];       // partial row sums of this lane's keys
+  bf16x8 qf[KK];     // Q^T fragments (B operand)
+  f32x16 oacc[DB];   // O^T accumulators: lane holds row l%32, 16 d values per block
+  float m_run;       // max used in the exponentials (log2 units)
+  float l_exact;     // this lane's partial sum of fp32 probabilities (for L)
+  float l_round;     // ... of the bf16-rounded probabilities (for O)
 };
 
-// Masked max of one row block's scores; returns the tile max in log2 units.
-template <bool MASK, bool CAUSAL>
-__device__ __forceinline__ float tile_rowmax(f32x16 (&s)[2], int j0, int qrow, int hi, int N, float c) {
+// Row max of one tile's scores (masked where needed), in log2 units.
+// lim: largest key offset (within the tile, minus the lane's 4*hi) that is visible.
+template <bool MASK>
+__device__ __forceinline__ float tile_rowmax(f32x16 (&s)[2], int lim, float c) {
   float mx = -INFINITY;
 #pragma unroll
   for (int a = 0; a < 2; ++a)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       if (MASK) {
-        const int key = j0 + a * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-        const bool vis = key < N && (!CAUSAL || key <= qrow);
-        s[a][r] = vis ? s[a][r] : -INFINITY;
+        const int koff = a * 32 + 8 * (r >> 2) + (r & 3);
+        s[a][r] = (koff <= lim) ? s[a][r] : -INFINITY;
       }
       mx = fmaxf(mx, s[a][r]);
     }
   mx = max_xor32(mx);
-  return (mx == -INFINITY) ? -INFINITY : mx * c;
+  return mx * c;  // c > 0, so -inf stays -inf
 }
 
-// Raise the running max of rows whose tile max exceeds it, rescaling that row
-// block's O and l.  Wave-uniform branch: skipped when no row of the wave grew.
+// Raise the running max of rows whose tile max exceeds it by more than the
+// threshold, rescaling O and the sums.  Wave-uniform branch.
 template <int D>
-__device__ __forceinline__ void maybe_rescale(WaveState<D>& st, int rb, float mt) {
-  const bool grow = mt > st.m_run[rb];
+__device__ __forceinline__ void maybe_rescale(WaveState<D>& st, float mt) {
+  const bool grow = mt > st.m_run + kRescaleThreshold;
   if (__builtin_amdgcn_ballot_w64(grow) != 0) {
-    const float mnew = fmaxf(st.m_run[rb], mt);
-    const float alpha = exp2_fast(st.m_run[rb] - mnew);  // m_run = -inf -> 0
-    st.l_run[rb] *= alpha;
+    const float mnew = fmaxf(st.m_run, mt);
+    const float alpha = exp2_fast(st.m_run - mnew);  // m_run = -inf -> 0
+    st.l_exact *= alpha;
+    st.l_round *= alpha;
 #pragma unroll
     for (int db = 0; db < WaveState<D>::DB; ++db)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) st.oacc[rb][db][r] *= alpha;
-    st.m_run[rb] = mnew;
+      for (int r = 0; r < 16; ++r) st.oacc[db][r] *= alpha;
+    st.m_run = mnew;
   }
 }
 
-// exp2 of the row block's scores against the running max, fp32 row sum, bf16 pack.
-template <bool MASK>
-__device__ __forceinline__ void softmax_pack(const f32x16 (&s)[2], float m, float c, float& l,
+// exp2 of the scores against the running max, packed to bf16 as the B operand of
+// the P V product; fp32 and bf16-rounded row sums.  Masked scores are -inf and
+// c > 0, so their probability is exactly 0.
+template <int D>
+__device__ __forceinline__ void softmax_pack(const f32x16 (&s)[2], WaveState<D>& st, float c,
                                              bf16x8 (&pb)[2][2]) {
-  const float mref = (m == -INFINITY) ? 0.f : m;
-  float psum = 0.f;
+  const float m = st.m_run;
+  const bf16x2 ones = as_bf16x2(0x3f803f80u);
+  float psum = 0.f, rsum = 0.f;
 #pragma unroll
   for (int a = 0; a < 2; ++a)
 #pragma unroll
-    for (int st = 0; st < 2; ++st) {
+    for (int h2 = 0; h2 < 2; ++h2) {
       u32x4 pk;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const float x0 = s[a][st * 8 + 2 * j], x1 = s[a][st * 8 + 2 * j + 1];
-        float p0 = exp2_fast(__builtin_fmaf(x0, c, -mref));
-        float p1 = exp2_fast(__builtin_fmaf(x1, c, -mref));
-        if (MASK) {
-          p0 = (x0 == -INFINITY) ? 0.f : p0;
-          p1 = (x1 == -INFINITY) ? 0.f : p1;
-        }
+        const float p0 = exp2_fast(__builtin_fmaf(s[a][h2 * 8 + 2 * j], c, -m));
+        const float p1 = exp2_fast(__builtin_fmaf(s[a][h2 * 8 + 2 * j + 1], c, -m));
         psum += p0;
         psum += p1;
-        pk[j] = pack_bf16x2(p0, p1);
+        const uint32_t w2 = pack_bf16x2(p0, p1);
+        rsum = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(w2), ones, rsum, false);
+        pk[j] = w2;
       }
-      pb[a][st] = __builtin_bit_cast(bf16x8, pk);
+      pb[a][h2] = __builtin_bit_cast(bf16x8, pk);
     }
-  l += psum;
+  st.l_exact += psum;
+  st.l_round += rsum;
 }
 
-template <int D, bool MASK, bool CAUSAL>
-__device__ __forceinline__ void process_tile(WaveState<D>& st, const uint8_t* kb, const uint8_t* vb, int j0,
-                                             int rw0, int lane, int N, float c) {
+template <int D, bool MASK>
+__device__ __forceinline__ void process_tile(WaveState<D>& st, const uint8_t* kb, const uint8_t* vb,
+                                             const int (&koff)[D / 16], const int (&voff)[D / 32], int lim,
+                                             int l32, float c) {
   using LY = Lay<D>;
   constexpr int KK = D / 16;
   constexpr int DB = D / 32;
-  const int l32 = lane & 31;
-  const int hi = lane >> 5;
 
-  // K fragments (A operand of S^T = K Q^T): key a*32 + l32, d = kk*16 + hi*8 .. +8
-  auto kfrag = [&](int a, int kk) {
-    const int r = a * 32 + l32;
-    return *reinterpret_cast<const bf16x8*>(kb + r * LY::ROWB + (((2 * kk + hi) ^ LY::swz_k(r)) << 4));
-  };
-  // V^T fragments (A operand of O^T = V^T P^T) through the transposing LDS read:
-  // keys a*32 + s2*16 + 4*hi + {0..3, 8..11}, d = db*32 + l32
-  const int grp = lane >> 4, li = lane & 15;
-  auto vaddr = [&](int r, int lc, int inner) {
-    return vb + r * LY::ROWB + ((lc ^ LY::swz_v(r)) << 4) + inner;
-  };
-  auto vfrag = [&](int a, int s2, int db) {
-    // source lane li reads 8 bytes of row kb1 + li/4 at d = dbase + 4*(li%4)
-    const int r = a * 32 + s2 * 16 + 4 * hi + (li >> 2);
-    const int lc = (db * 32 + (grp & 1) * 16) / 8 + ((li & 3) >> 1);
-    const int inner = (li & 1) * 8;
-    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS s16x4*)(vaddr(r, lc, inner)));
-    const s16x4 up = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS s16x4*)(vaddr(r + 8, lc, inner)));
-    const s16x8 cat = __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7);
-    return __builtin_bit_cast(bf16x8, cat);
-  };
-
-  // ---- scores S^T = K Q^T for every row block
-  f32x16 sc[kRB][2];
+  // ---- scores S^T = K Q^T; K fragment: key a*32 + l32, d = kk*16 + hi*8 .. +8
+  f32x16 sc[2];
 #pragma unroll
-  for (int rb = 0; rb < kRB; ++rb)
+  for (int a = 0; a < 2; ++a)
 #pragma unroll
-    for (int a = 0; a < 2; ++a)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) sc[rb][a][r] = 0.f;
+    for (int r = 0; r < 16; ++r) sc[a][r] = 0.f;
 #pragma unroll
   for (int kk = 0; kk < KK; ++kk)
 #pragma unroll
     for (int a = 0; a < 2; ++a) {
-      const bf16x8 kf = kfrag(a, kk);
-#pragma unroll
-      for (int rb = 0; rb < kRB; ++rb)
-        sc[rb][a] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, st.qf[rb][kk], sc[rb][a], 0, 0, 0);
+      const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kb + (a * 32 + l32) * LY::ROWB + koff[kk]);
+      sc[a] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, st.qf[kk], sc[a], 0, 0, 0);
     }
 
-  // ---- online softmax per row block
-  bf16x8 pb[kRB][2][2];
-#pragma unroll
-  for (int rb = 0; rb < kRB; ++rb) {
-    const float mt = tile_rowmax<MASK, CAUSAL>(sc[rb], j0, rw0 + 32 * rb + l32, hi, N, c);
-    maybe_rescale<D>(st, rb, mt);
-    softmax_pack<MASK>(sc[rb], st.m_run[rb], c, st.l_run[rb], pb[rb]);
-  }
+  // ---- online softmax
+  const float mt = tile_rowmax<MASK>(sc, lim, c);
+  maybe_rescale<D>(st, mt);
+  bf16x8 pb[2][2];
+  softmax_pack<D>(sc, st, c, pb);
 
-  // ---- O^T += V^T P^T
+  // ---- O^T += V^T P^T.  V^T fragment for (a, h2, db): keys a*32 + h2*16 + 4*hi +
+  // {0..3, 8..11}, d = db*32 + l32, via two transposing reads of 4 keys each
+  // (voff[db] holds this lane's row-in-group and swizzled chunk offset).
   // (scheduling fence: the V fragment reads are not hoisted into the score phase,
   // where their registers would push the wave past its 256-register budget)
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int a = 0; a < 2; ++a)
 #pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2)
+    for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        const bf16x8 vf = vfrag(a, s2, db);
-#pragma unroll
-        for (int rb = 0; rb < kRB; ++rb)
-          st.oacc[rb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[rb][a][s2], st.oacc[rb][db], 0, 0, 0);
+        const uint8_t* p1 = vb + (a * 32 + h2 * 16) * LY::ROWB + voff[db];
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS s16x4*)(p1));
+        const s16x4 up = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS s16x4*)(p1 + 8 * LY::ROWB));
+        const s16x8 cat = __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7);
+        st.oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, cat), pb[a][h2],
+                                                              st.oacc[db], 0, 0, 0);
       }
+}
+
+// HBM -> LDS copy of one K/V tile into buffer buf: this wave's 1 KB blocks
+// w, w + 8, ... of each tensor; kcp/vcp are the lane's byte offsets within the
+// tile's rows (swizzle included), to which the tile's first-row offset is added.
+// The buffer descriptors span one head's K (V) rows, so rows past N read as zero.
+template <int D>
+__device__ __forceinline__ void copy_tile(uint8_t* smem, const void* kbase, const void* vbase, uint32_t head_bytes,
+                                          const uint32_t* kcp, const uint32_t* vcp,
+                                          int j0, int buf, int w) {
+  using LY = Lay<D>;
+  const auto krs = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(kbase), (short)0, head_bytes, 0x00020000);
+  const auto vrs = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(vbase), (short)0, head_bytes, 0x00020000);
+  uint8_t* kb = smem + buf * LY::BUF;
+  uint8_t* vb = kb + LY::TBYTES;
+  const uint32_t base = (uint32_t)j0 * LY::ROWB;
+#pragma unroll
+  for (int i = 0; i < LY::BPW; ++i) {
+    const int blk = w + kWaves * i;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (FA_LDS void*)(kb + blk * 1024), 16, base + kcp[i], 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (FA_LDS void*)(vb + blk * 1024), 16, base + vcp[i], 0, 0, 0);
+  }
 }
 
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     uint16_t* __restrict__ O, float* __restrict__ Lse, int B, int Hq, int Hkv, int N,
-    float c /* |scale| * log2(e) */, uint32_t qsign /* 0x80008000 if scale < 0 */) {
+    float c /* |scale| * log2(e), > 0 */, uint32_t qsign /* 0x80008000 if scale < 0 */) {
   using LY = Lay<D>;
   constexpr int KK = D / 16;
   constexpr int DB = D / 32;
@@ -244,63 +251,62 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
   const int lane = tid & 63;
   const int l32 = lane & 31;
   const int hi = lane >> 5;  // which half of the wave
+  const int grp = lane >> 4, li = lane & 15;
   const int rw0 = qb * kBR + w * kRowsPerWave;
+  const int qrow = rw0 + l32;
 
   const uint16_t* qbase = Q + ((size_t)(b * Hq + h) * N) * D;
   const uint16_t* kbase = K + ((size_t)(b * Hkv + g) * N) * D;
   const uint16_t* vbase = V + ((size_t)(b * Hkv + g) * N) * D;
 
   WaveState<D> st;
-  // Q fragments (B operand of S^T = K Q^T): row rw0 + rb*32 + l32, d = kk*16 + hi*8 .. +8
+  // Q fragments (B operand of S^T = K Q^T): row qrow, d = kk*16 + hi*8 .. +8
 #pragma unroll
-  for (int rb = 0; rb < kRB; ++rb) {
-    const int row = rw0 + rb * 32 + l32;
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      u32x4 x = {0u, 0u, 0u, 0u};
-      if (row < N) x = ld_global16(qbase + (size_t)row * D + kk * 16 + hi * 8);
-      x ^= qsign;
-      st.qf[rb][kk] = __builtin_bit_cast(bf16x8, x);
-    }
+  for (int kk = 0; kk < KK; ++kk) {
+    u32x4 x = {0u, 0u, 0u, 0u};
+    if (qrow < N) x = ld_global16(qbase + (size_t)qrow * D + kk * 16 + hi * 8);
+    x ^= qsign;
+    st.qf[kk] = __builtin_bit_cast(bf16x8, x);
   }
 #pragma unroll
-  for (int rb = 0; rb < kRB; ++rb) {
+  for (int db = 0; db < DB; ++db)
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
+    for (int r = 0; r < 16; ++r) st.oacc[db][r] = 0.f;
+  st.m_run = -INFINITY;
+  st.l_exact = 0.f;
+  st.l_round = 0.f;
+
+  // loop-invariant LDS byte offsets of this lane's fragment reads
+  int koff[KK], voff[DB];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) st.oacc[rb][db][r] = 0.f;
-    st.m_run[rb] = -INFINITY;
-    st.l_run[rb] = 0.f;
+  for (int kk = 0; kk < KK; ++kk) koff[kk] = ((2 * kk + hi) ^ LY::swz_k(l32)) << 4;
+  {
+    const int vr = 4 * hi + (li >> 2);  // row within a 16-key step (the +8 read keeps the swizzle)
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const int lc = 4 * db + 2 * (grp & 1) + ((li & 3) >> 1);
+      voff[db] = vr * LY::ROWB + ((lc ^ LY::swz_v(vr)) << 4) + (li & 1) * 8;
+    }
   }
 
   const int kend = CAUSAL ? min(N, (qb + 1) * kBR) : N;
   const int ntiles = (kend + kBC - 1) / kBC;
 
   // ---- HBM -> LDS copies of one K/V tile (buffer loads with the LDS bit).  Wave w
-  // copies 1 KB blocks w, w + 4, ... of each tensor; lane l of a block writes
+  // copies 1 KB blocks w, w + 8, ... of each tensor; lane l of a block writes
   // physical chunk l % CPR of row blk*RPB + l / CPR, which holds logical chunk
-  // (l % CPR) ^ swz(row).  Out-of-range rows (key >= N) read as zero.
+  // (l % CPR) ^ swz(row).  Rows past N lie past the buffer end and read as zero.
   const uint32_t head_bytes = (uint32_t)N * D * 2;
-  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void*)kbase, (short)0, head_bytes, 0x00020000);
-  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void*)vbase, (short)0, head_bytes, 0x00020000);
-  auto copy_tile = [&](int j0, int buf) {
-    uint8_t* kb = smem + buf * LY::BUF;
-    uint8_t* vb = kb + LY::TBYTES;
+  uint32_t kcp[LY::BPW], vcp[LY::BPW];
 #pragma unroll
-    for (int i = 0; i < LY::BPW; ++i) {
-      const int blk = w + kWaves * i;
-      const int r = blk * LY::RPB + lane / LY::CPR;
-      const int pc = lane % LY::CPR;
-      const uint32_t row_off = (uint32_t)(j0 + r) * (D * 2);
-      // a row past N gets an offset past the buffer end, so the copy writes zeros
-      const uint32_t koff = (j0 + r < N) ? row_off + ((pc ^ LY::swz_k(r)) << 4) : head_bytes;
-      const uint32_t voff = (j0 + r < N) ? row_off + ((pc ^ LY::swz_v(r)) << 4) : head_bytes;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (FA_LDS void*)(kb + blk * 1024), 16, koff, 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (FA_LDS void*)(vb + blk * 1024), 16, voff, 0, 0, 0);
-    }
-  };
-
-  copy_tile(0, 0);
+  for (int i = 0; i < LY::BPW; ++i) {
+    const int blk = w + kWaves * i;
+    const int r = blk * LY::RPB + lane / LY::CPR;
+    const int pc = lane % LY::CPR;
+    kcp[i] = r * LY::ROWB + ((pc ^ LY::swz_k(r)) << 4);
+    vcp[i] = r * LY::ROWB + ((pc ^ LY::swz_v(r)) << 4);
+  }
+  copy_tile<D>(smem, kbase, vbase, head_bytes, kcp, vcp, 0, 0, w);
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies have landed
   __syncthreads();
 
@@ -308,43 +314,43 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
     const int buf = t & 1;
     const int j0 = t * kBC;
     // the other buffer was last read in tile t - 1, which every wave has finished
-    if (t + 1 < ntiles) copy_tile(j0 + kBC, buf ^ 1);
+    if (t + 1 < ntiles) copy_tile<D>(smem, kbase, vbase, head_bytes, kcp, vcp, j0 + kBC, buf ^ 1, w);
 
     const bool skip = CAUSAL && (j0 > rw0 + kRowsPerWave - 1);
     if (!skip) {
-      const bool need_mask = (CAUSAL && (j0 + kBC - 1 > rw0)) || (j0 + kBC > N);
+      const bool need_mask = CAUSAL ? (j0 + kBC - 1 > rw0) : (j0 + kBC > N);
+      // causal: key j0 + koff visible iff koff + 4*hi <= qrow - j0 (keys past N
+      // only reach rows >= N, which are never stored); otherwise iff key < N
+      const int lim = (CAUSAL ? qrow - j0 : N - 1 - j0) - 4 * hi;
       const uint8_t* kb = smem + buf * LY::BUF;
       const uint8_t* vb = kb + LY::TBYTES;
       if (need_mask)
-        process_tile<D, true, CAUSAL>(st, kb, vb, j0, rw0, lane, N, c);
+        process_tile<D, true>(st, kb, vb, koff, voff, lim, l32, c);
       else
-        process_tile<D, false, CAUSAL>(st, kb, vb, j0, rw0, lane, N, c);
+        process_tile<D, false>(st, kb, vb, koff, voff, lim, l32, c);
     }
 
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     __syncthreads();
   }
 
-  // ---- epilogue: O = O / l (bf16), L = (m + log2 l) ln 2
+  // ---- epilogue: O = O / l_round (bf16), L = (m + log2 l_exact) ln 2
+  const float lr = sum_xor32(st.l_round);
+  const float le = sum_xor32(st.l_exact);
+  const float inv = 1.f / lr;
+  if (qrow < N) {
+    uint16_t* orow = O + ((size_t)(b * Hq + h) * N + qrow) * D;
 #pragma unroll
-  for (int rb = 0; rb < kRB; ++rb) {
-    const float lt = sum_xor32(st.l_run[rb]);
-    const float inv = 1.f / lt;
-    const int row = rw0 + rb * 32 + l32;
-    if (row < N) {
-      uint16_t* orow = O + ((size_t)(b * Hq + h) * N + row) * D;
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          const int d0 = db * 32 + 8 * g4 + 4 * hi;
-          u32x2 w2;
-          w2[0] = pack_bf16x2(st.oacc[rb][db][4 * g4 + 0] * inv, st.oacc[rb][db][4 * g4 + 1] * inv);
-          w2[1] = pack_bf16x2(st.oacc[rb][db][4 * g4 + 2] * inv, st.oacc[rb][db][4 * g4 + 3] * inv);
-          *reinterpret_cast<u32x2*>(orow + d0) = w2;
-        }
-      if (hi == 0) Lse[(size_t)(b * Hq + h) * N + row] = (st.m_run[rb] + log2_fast(lt)) * kLn2;
-    }
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d0 = db * 32 + 8 * g4 + 4 * hi;
+        u32x2 w2;
+        w2[0] = pack_bf16x2(st.oacc[db][4 * g4 + 0] * inv, st.oacc[db][4 * g4 + 1] * inv);
+        w2[1] = pack_bf16x2(st.oacc[db][4 * g4 + 2] * inv, st.oacc[db][4 * g4 + 3] * inv);
+        *reinterpret_cast<u32x2*>(orow + d0) = w2;
+      }
+    if (hi == 0) Lse[(size_t)(b * Hq + h) * N + qrow] = (st.m_run + log2_fast(le)) * kLn2;
   }
 }
 
@@ -352,7 +358,10 @@ template <int D, bool CAUSAL>
 hipError_t launch(const FwdArgs& a) {
   const int nqb = (a.N + kBR - 1) / kBR;
   const dim3 grid((unsigned)(nqb * a.B * a.Hq));
-  const float c = fabsf(a.scale) * kLog2e;
+  // scores are used as s * c with c > 0; a zero scale becomes a tiny positive c,
+  // which leaves every unmasked exponential exactly 1 and masked ones exactly 0
+  float c = fabsf(a.scale) * kLog2e;
+  if (!(c > 1e-30f)) c = 1e-30f;
   const uint32_t qsign = a.scale < 0.f ? 0x80008000u : 0u;
   hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL>), grid, dim3(kThreads), 0, (hipStream_t)a.stream,
                      (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o,
