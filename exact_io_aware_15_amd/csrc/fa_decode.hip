@@ -56,7 +56,9 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
   const int p_end = min(npages, p_begin + kDecodePagesPerSplit);
 
   const int tid = threadIdx.x;
-  const int w = tid >> 6;
+  // wave index made provably wave-uniform, so page ids below are read with scalar
+  // loads (their waits do not drain the in-flight K/V vector loads)
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int tg = lane >> 3;  // token pair within the page
   const int dg = lane & 7;   // column group

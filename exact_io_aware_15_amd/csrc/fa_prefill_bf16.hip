@@ -46,11 +46,18 @@ namespace fa {
 namespace {
 
 constexpr int kRowsPerWave = 32;            // one 32-row MFMA block per wave
-constexpr int kWaves = 8;                   // two waves per SIMD
+#ifndef FA_PREFILL_WAVES
+#define FA_PREFILL_WAVES 8
+#endif
+constexpr int kWaves = FA_PREFILL_WAVES;    // waves per workgroup (8: two per SIMD)
 constexpr int kThreads = kWaves * 64;
 constexpr int kBR = kWaves * kRowsPerWave;  // 256 query rows per workgroup
 constexpr int kBC = 64;                     // keys per tile (two 32-key MFMA blocks)
 constexpr float kRescaleThreshold = 8.0f;   // log2 units: probabilities stay <= 256
+#ifndef FA_PREFILL_STAGES
+#define FA_PREFILL_STAGES 2
+#endif
+constexpr int kStages = FA_PREFILL_STAGES;  // K/V tiles resident in LDS (copies run kStages-1 ahead)
 
 template <int D>
 struct Lay {
@@ -58,7 +65,6 @@ struct Lay {
   static constexpr int CPR = ROWB / 16;         // 16-byte chunks per row
   static constexpr int RPB = 1024 / ROWB;       // rows per 1 KB wave copy (64 lanes x 16 B)
   static constexpr int TBYTES = kBC * ROWB;     // one tensor tile
-  static constexpr int BUF = 2 * TBYTES;        // K tile then V tile
   static constexpr int BLOCKS = TBYTES / 1024;  // 1 KB copies per tensor tile
   static constexpr int BPW = BLOCKS / kWaves;   // ... per wave
   static_assert(BPW * kWaves == BLOCKS, "tile copy must split evenly over the waves");
@@ -77,6 +83,21 @@ __device__ __forceinline__ u32x4 ld_global16(const void* p) {
 }
 
 typedef short s16x8 __attribute__((ext_vector_type(8)));
+
+// s_waitcnt vmcnt(n * L): wait until at most n tiles' worth (L loads each) of this
+// wave's HBM -> LDS copies are outstanding.  n is 0 .. kStages-2.
+template <int L>
+__device__ __forceinline__ void wait_vmem_tiles(int n) {
+  static_assert(L * (kStages - 2) < 64, "vmcnt field is 6 bits");
+  auto enc = [](int v) { return 0x0F70 | (v & 15) | ((v >> 4) << 14); };
+  if (kStages > 3 && n >= 2) {
+    __builtin_amdgcn_s_waitcnt(enc(2 * L));
+  } else if (kStages > 2 && n == 1) {
+    __builtin_amdgcn_s_waitcnt(enc(L));
+  } else {
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+  }
+}
 
 // Per-wave state carried across tiles.
 template <int D>
@@ -217,8 +238,9 @@ __device__ __forceinline__ void copy_tile(uint8_t* smem, const void* kbase, cons
   using LY = Lay<D>;
   const auto krs = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(kbase), (short)0, head_bytes, 0x00020000);
   const auto vrs = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(vbase), (short)0, head_bytes, 0x00020000);
-  uint8_t* kb = smem + buf * LY::BUF;
-  uint8_t* vb = kb + LY::TBYTES;
+  // LDS slots: K tiles in slots 0 .. kStages-1, V tiles in slots kStages .. 2*kStages-1
+  uint8_t* kb = smem + buf * LY::TBYTES;
+  uint8_t* vb = smem + (kStages + buf) * LY::TBYTES;
   const uint32_t base = (uint32_t)j0 * LY::ROWB;
 #pragma unroll
   for (int i = 0; i < LY::BPW; ++i) {
@@ -229,14 +251,14 @@ __device__ __forceinline__ void copy_tile(uint8_t* smem, const void* kbase, cons
 }
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
+__global__ __launch_bounds__(kThreads, 8 / kWaves) void fwd_bf16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     uint16_t* __restrict__ O, float* __restrict__ Lse, int B, int Hq, int Hkv, int N,
     float c /* |scale| * log2(e), > 0 */, uint32_t qsign /* 0x80008000 if scale < 0 */) {
   using LY = Lay<D>;
   constexpr int KK = D / 16;
   constexpr int DB = D / 32;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * LY::BUF];
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kStages * LY::TBYTES];
 
   const int nqb = (N + kBR - 1) / kBR;
   const int BH = B * Hq;
@@ -306,32 +328,49 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
     kcp[i] = r * LY::ROWB + ((pc ^ LY::swz_k(r)) << 4);
     vcp[i] = r * LY::ROWB + ((pc ^ LY::swz_v(r)) << 4);
   }
-  copy_tile<D>(smem, kbase, vbase, head_bytes, kcp, vcp, 0, 0, w);
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies have landed
+  // LDS ring of kStages tiles: tile t lives in slot t % kStages, and the copy of
+  // tile t + kStages - 1 is started at the top of iteration t into the slot that
+  // tile t - 1 used (every wave finished it before the previous barrier).  Each
+  // wave waits only for the copies of the tile needed next (vmcnt counts this
+  // wave's outstanding loads in issue order), so a copy has kStages - 1 tile-times
+  // to arrive from HBM.
+  constexpr int kLoadsPerTile = 2 * LY::BPW;
+#pragma unroll
+  for (int p = 0; p < kStages - 1; ++p)
+    if (p < ntiles) copy_tile<D>(smem, kbase, vbase, head_bytes, kcp, vcp, p * kBC, p, w);
+  wait_vmem_tiles<kLoadsPerTile>(min(kStages - 2, ntiles - 1));  // tile 0 has landed
   __syncthreads();
 
-  for (int t = 0; t < ntiles; ++t) {
-    const int buf = t & 1;
-    const int j0 = t * kBC;
-    // the other buffer was last read in tile t - 1, which every wave has finished
-    if (t + 1 < ntiles) copy_tile<D>(smem, kbase, vbase, head_bytes, kcp, vcp, j0 + kBC, buf ^ 1, w);
+  // The loop is unrolled by kStages so every slot index, and with it every LDS
+  // address offset, is a compile-time constant.
+  for (int t0 = 0; t0 < ntiles; t0 += kStages) {
+#pragma unroll
+    for (int u = 0; u < kStages; ++u) {
+      const int t = t0 + u;
+      if (t >= ntiles) break;
+      const int j0 = t * kBC;
+      if (t + kStages - 1 < ntiles)
+        copy_tile<D>(smem, kbase, vbase, head_bytes, kcp, vcp, j0 + (kStages - 1) * kBC, (u + kStages - 1) % kStages,
+                     w);
 
-    const bool skip = CAUSAL && (j0 > rw0 + kRowsPerWave - 1);
-    if (!skip) {
-      const bool need_mask = CAUSAL ? (j0 + kBC - 1 > rw0) : (j0 + kBC > N);
-      // causal: key j0 + koff visible iff koff + 4*hi <= qrow - j0 (keys past N
-      // only reach rows >= N, which are never stored); otherwise iff key < N
-      const int lim = (CAUSAL ? qrow - j0 : N - 1 - j0) - 4 * hi;
-      const uint8_t* kb = smem + buf * LY::BUF;
-      const uint8_t* vb = kb + LY::TBYTES;
-      if (need_mask)
-        process_tile<D, true>(st, kb, vb, koff, voff, lim, l32, c);
-      else
-        process_tile<D, false>(st, kb, vb, koff, voff, lim, l32, c);
+      const bool skip = CAUSAL && (j0 > rw0 + kRowsPerWave - 1);
+      if (!skip) {
+        const bool need_mask = CAUSAL ? (j0 + kBC - 1 > rw0) : (j0 + kBC > N);
+        // causal: key j0 + koff visible iff koff + 4*hi <= qrow - j0 (keys past N
+        // only reach rows >= N, which are never stored); otherwise iff key < N
+        const int lim = (CAUSAL ? qrow - j0 : N - 1 - j0) - 4 * hi;
+        const uint8_t* kb = smem + u * LY::TBYTES;
+        const uint8_t* vb = smem + (kStages + u) * LY::TBYTES;
+        if (need_mask)
+          process_tile<D, true>(st, kb, vb, koff, voff, lim, l32, c);
+        else
+          process_tile<D, false>(st, kb, vb, koff, voff, lim, l32, c);
+      }
+
+      // tile t + 1 must have landed; the copies of later tiles may still be in flight
+      wait_vmem_tiles<kLoadsPerTile>(max(0, min(kStages - 2, ntiles - 2 - t)));
+      __syncthreads();
     }
-
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-    __syncthreads();
   }
 
   // ---- epilogue: O = O / l_round (bf16), L = (m + log2 l_exact) ln 2
