@@ -3,7 +3,7 @@
 // table ("Phase 08 -- Inference Optimization at Depth", Concepts list: KV cache,
 // paged attention; Lab 03 steps 1 and 4).
 //
-// Phase 1 (decode_split_kernel): one workgroup per (split of 32 pages, K/V head,
+// Phase 1 (decode_split_kernel): one workgroup per (split of 64 pages, K/V head,
 // sequence) serves up to HB query heads of that K/V head's group, so each K/V
 // page is read from HBM once for the whole group.  Its 4 waves take the split's
 // pages two at a time, round-robin.  In a wave, lane l holds tokens 2*(l/8) and
@@ -42,6 +42,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
   constexpr int PP = 2;        // pages consumed per wave iteration
   __shared__ float sm_m[kDecWaves][HB];
   __shared__ float sm_l[kDecWaves][HB];
+  __shared__ float sm_lr[kDecWaves][HB];
   __shared__ float sm_acc[kDecWaves][HB][D];
 
   const int split = blockIdx.x;
@@ -81,11 +82,15 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
     qscale[hh] = c;
   }
 
-  float m_run[HB], l_run[HB], acc[HB][DL];
+  // online-softmax state per served head: running max (log2 units), sums of the
+  // fp32 probabilities (for L) and of their bf16 roundings (for O), and the
+  // unnormalised output accumulator for this lane's d columns
+  float m_run[HB], l_run[HB], l_rnd[HB], acc[HB][DL];
 #pragma unroll
   for (int hh = 0; hh < HB; ++hh) {
     m_run[hh] = -INFINITY;
     l_run[hh] = 0.f;
+    l_rnd[hh] = 0.f;
 #pragma unroll
     for (int i = 0; i < DL; ++i) acc[hh][i] = 0.f;
   }
@@ -94,34 +99,31 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
   const size_t head_off = (size_t)g * kPage * D;
   const size_t page_stride = (size_t)Hkv * kPage * D;
 
-  // register buffers: [page of the pair][token of the lane][chunk]
-  u32x4 kc[PP][2][CPL], vc[PP][2][CPL];
-  u32x4 kn[PP][2][CPL], vn[PP][2][CPL];
+  // Two register buffers (A, B) of one page pair each, used alternately: the pair
+  // after next is fetched into the buffer just consumed, so one pair is always in
+  // flight while the other is processed (no register copies that would force a
+  // wait on outstanding loads).
+  u32x4 ka[PP][2][CPL], va[PP][2][CPL];
+  u32x4 kb[PP][2][CPL], vb[PP][2][CPL];
+  // Loads are unconditional (so the compiler keeps the other buffer's loads in
+  // flight across the waits): a page past this split's end is redirected to the
+  // split's last page, and its tokens are treated as invalid by consume().
   auto fetch = [&](int p0, u32x4 (&kd)[PP][2][CPL], u32x4 (&vd)[PP][2][CPL]) {
 #pragma unroll
     for (int pp = 0; pp < PP; ++pp) {
-      const int p = p0 + pp;
-      const bool have = p < p_end;
-      const size_t base = (size_t)trow[have ? p : p0] * page_stride + head_off;
+      const int p = min(p0 + pp, p_end - 1);
+      const size_t base = (size_t)trow[p] * page_stride + head_off;
 #pragma unroll
       for (int j = 0; j < 2; ++j)
 #pragma unroll
         for (int cc = 0; cc < CPL; ++cc) {
           const size_t off = base + (size_t)(2 * tg + j) * D + (dg + 8 * cc) * 8;
-          const u32x4 z = {0u, 0u, 0u, 0u};
-          kd[pp][j][cc] = have ? ldg16(KPg + off) : z;
-          vd[pp][j][cc] = have ? ldg16(VPg + off) : z;
+          kd[pp][j][cc] = ldg16(KPg + off);
+          vd[pp][j][cc] = ldg16(VPg + off);
         }
     }
   };
-
-  // wave w takes page pairs (p_begin + PP*w, +1), (p_begin + PP*(w + 4), +1), ...
-  int p = p_begin + PP * w;
-  if (p < p_end) fetch(p, kc, vc);
-  for (; p < p_end; p += PP * kDecWaves) {
-    const int pn = p + PP * kDecWaves;
-    if (pn < p_end) fetch(pn, kn, vn);
-
+  auto consume = [&](int p, u32x4 (&kc)[PP][2][CPL], u32x4 (&vc)[PP][2][CPL]) {
     // scores: this lane's 2 tokens of each page of the pair, every served head
     float sc[PP][2][HB];
 #pragma unroll
@@ -129,7 +131,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const int tok = (p + pp) * kPage + 2 * tg + j;
-        const bool valid = tok < n;
+        const bool valid = tok < n && p + pp < p_end;
 #pragma unroll
         for (int hh = 0; hh < HB; ++hh) {
           float part = 0.f;
@@ -158,58 +160,79 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
       for (int hh = 0; hh < HB; ++hh) {
         const float alpha = exp2_fast(m_run[hh] - mnew[hh]);
         l_run[hh] *= alpha;
+        l_rnd[hh] *= alpha;
 #pragma unroll
         for (int i = 0; i < DL; ++i) acc[hh][i] *= alpha;
         m_run[hh] = mnew[hh];
       }
     }
-    // the sequence's last page may hold slots past ctx_len: zero their V so that
-    // 0 * NaN cannot occur
-    if ((p + PP) * kPage > n) {
+    // the sequence's last page may hold slots past ctx_len (and a redirected page
+    // is a duplicate): zero their V so that 0 * NaN cannot occur
+    if ((p + PP) * kPage > n || p + PP > p_end) {
 #pragma unroll
       for (int pp = 0; pp < PP; ++pp)
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-          const bool valid = (p + pp) * kPage + 2 * tg + j < n;
+          const bool valid = (p + pp) * kPage + 2 * tg + j < n && p + pp < p_end;
 #pragma unroll
           for (int cc = 0; cc < CPL; ++cc)
 #pragma unroll
             for (int e = 0; e < 4; ++e) vc[pp][j][cc][e] = valid ? vc[pp][j][cc][e] : 0u;
         }
     }
+    // O += P V as bf16 pair dot products over the lane's two tokens: P packed as
+    // (p(t0), p(t1)) per head, V repacked as (V[t0][d], V[t1][d]) per column.  O is
+    // later divided by the sum of these rounded probabilities, L uses the fp32 sum.
+    const bf16x2 ones = as_bf16x2(0x3f803f80u);
 #pragma unroll
-    for (int pp = 0; pp < PP; ++pp)
+    for (int pp = 0; pp < PP; ++pp) {
+      uint32_t ppair[HB];
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+      for (int hh = 0; hh < HB; ++hh) {
+        const float p0 = (sc[pp][0][hh] == -INFINITY) ? 0.f : exp2_fast(sc[pp][0][hh] - m_run[hh]);
+        const float p1 = (sc[pp][1][hh] == -INFINITY) ? 0.f : exp2_fast(sc[pp][1][hh] - m_run[hh]);
+        l_run[hh] += p0 + p1;
+        ppair[hh] = pack_bf16x2(p0, p1);
+        l_rnd[hh] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(ppair[hh]), ones, l_rnd[hh], false);
+      }
 #pragma unroll
-        for (int hh = 0; hh < HB; ++hh) {
-          const float pr = (sc[pp][j][hh] == -INFINITY) ? 0.f : exp2_fast(sc[pp][j][hh] - m_run[hh]);
-          l_run[hh] += pr;
+      for (int cc = 0; cc < CPL; ++cc)
 #pragma unroll
-          for (int cc = 0; cc < CPL; ++cc)
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t w0 = vc[pp][0][cc][e], w1 = vc[pp][1][cc][e];
+          const uint32_t lo = __builtin_amdgcn_perm(w1, w0, 0x05040100u);  // (w0.lo, w1.lo)
+          const uint32_t hi = __builtin_amdgcn_perm(w1, w0, 0x07060302u);  // (w0.hi, w1.hi)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              acc[hh][cc * 8 + 2 * e] =
-                  __builtin_fmaf(pr, bf16lo_to_f32(vc[pp][j][cc][e]), acc[hh][cc * 8 + 2 * e]);
-              acc[hh][cc * 8 + 2 * e + 1] =
-                  __builtin_fmaf(pr, bf16hi_to_f32(vc[pp][j][cc][e]), acc[hh][cc * 8 + 2 * e + 1]);
-            }
+          for (int hh = 0; hh < HB; ++hh) {
+            acc[hh][cc * 8 + 2 * e] =
+                __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(ppair[hh]), as_bf16x2(lo), acc[hh][cc * 8 + 2 * e], false);
+            acc[hh][cc * 8 + 2 * e + 1] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(ppair[hh]), as_bf16x2(hi),
+                                                                          acc[hh][cc * 8 + 2 * e + 1], false);
+          }
         }
-#pragma unroll
-    for (int pp = 0; pp < PP; ++pp)
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int cc = 0; cc < CPL; ++cc) {
-          kc[pp][j][cc] = kn[pp][j][cc];
-          vc[pp][j][cc] = vn[pp][j][cc];
-        }
+    }
+  };
+
+  // wave w takes page pairs p_begin + PP*(w + 4i), i = 0, 1, ...
+  constexpr int kStride = PP * kDecWaves;
+  int p = p_begin + PP * w;
+  if (p < p_end) fetch(p, ka, va);
+  // (the prefetch after a wave's last pair re-reads that pair, from L2)
+  while (p < p_end) {
+    fetch(p + kStride < p_end ? p + kStride : p, kb, vb);
+    consume(p, ka, va);
+    p += kStride;
+    if (p >= p_end) break;
+    fetch(p + kStride < p_end ? p + kStride : p, ka, va);
+    consume(p, kb, vb);
+    p += kStride;
   }
 
   // combine the 8 token-pair lanes of each column group, then the 4 waves
 #pragma unroll
   for (int hh = 0; hh < HB; ++hh) {
     l_run[hh] = sum_stride8(l_run[hh]);
+    l_rnd[hh] = sum_stride8(l_rnd[hh]);
 #pragma unroll
     for (int i = 0; i < DL; ++i) acc[hh][i] = sum_stride8(acc[hh][i]);
   }
@@ -219,6 +242,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
       if (lane == 0) {
         sm_m[w][hh] = m_run[hh];
         sm_l[w][hh] = l_run[hh];
+        sm_lr[w][hh] = l_rnd[hh];
       }
 #pragma unroll
       for (int cc = 0; cc < CPL; ++cc)
@@ -234,16 +258,17 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
     float M = -INFINITY;
 #pragma unroll
     for (int ww = 0; ww < kDecWaves; ++ww) M = fmaxf(M, sm_m[ww][hh]);
-    float wsum = 0.f, o = 0.f;
+    float wsum = 0.f, rsum = 0.f, o = 0.f;
 #pragma unroll
     for (int ww = 0; ww < kDecWaves; ++ww) {
       const float mw = sm_m[ww][hh];
       const float f = (mw == -INFINITY) ? 0.f : exp2_fast(mw - M);
       wsum += f * sm_l[ww][hh];
+      rsum += f * sm_lr[ww][hh];
       o += f * sm_acc[ww][hh][d];
     }
     const size_t slot = ((size_t)s * Hq + g * G + hl) * max_splits + split;
-    ws_o[slot * D + d] = o / wsum;
+    ws_o[slot * D + d] = o / rsum;
     if (d == 0) ws_l[slot] = M + log2_fast(wsum);  // log2 units
   }
 }

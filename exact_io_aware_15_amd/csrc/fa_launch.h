@@ -35,7 +35,10 @@ struct DecodeArgs {
 };
 
 // Pages handled by one split of the paged decode.  The workspace size depends on it.
-constexpr int kDecodePagesPerSplit = 32;
+#ifndef FA_DECODE_PAGES_PER_SPLIT
+#define FA_DECODE_PAGES_PER_SPLIT 64
+#endif
+constexpr int kDecodePagesPerSplit = FA_DECODE_PAGES_PER_SPLIT;
 
 inline int decode_max_splits(int max_pages) {
   return (max_pages + kDecodePagesPerSplit - 1) / kDecodePagesPerSplit;

@@ -96,9 +96,9 @@ def test_decode_validation(L):
 
 
 def test_workspace_size(L):
-    # one fp32 partial (d values + one logsumexp) per (sequence, head, split of 32 pages)
+    # one fp32 partial (d values + one logsumexp) per (sequence, head, split of 64 pages)
     for S, Hq, d, maxp in [(64, 32, 128, 1024), (1, 1, 64, 1), (3, 4, 64, 33)]:
-        splits = -(-maxp // 32)
+        splits = -(-maxp // 64)
         o_bytes = S * Hq * splits * d * 4
         assert fa.fa_decode_paged_workspace_size(S, Hq, d, maxp, 16) == -(-o_bytes // 256) * 256 + S * Hq * splits * 4
     assert fa.fa_decode_paged_workspace_size(1, 1, 96, 1, 16) == 0
