@@ -91,7 +91,9 @@ int fa_decode_paged(const void* q, const void* kpages, const void* vpages, const
                     size_t workspace_bytes, void* stream) {
   if (num_seqs < 0 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || max_pages_per_seq < 1 || num_pages < 1)
     return FA_ERR_SHAPE;
-  if ((long long)num_seqs * Hq > 0x7fffffffLL || num_seqs > 65535) return FA_ERR_SHAPE;
+  // grid: x = num_seqs * Hkv * ceil(G / heads per workgroup) <= num_seqs * Hq; y = splits
+  if ((long long)num_seqs * Hq > 0x7fffffffLL || fa::decode_max_splits(max_pages_per_seq) > 65535)
+    return FA_ERR_SHAPE;
   if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
   if (page_size != 16) return FA_ERR_UNSUPPORTED;
   if (!std::isfinite(scale)) return FA_ERR_SCALE;

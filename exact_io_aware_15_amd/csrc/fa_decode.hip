@@ -3,10 +3,16 @@
 // table ("Phase 08 -- Inference Optimization at Depth", Concepts list: KV cache,
 // paged attention; Lab 03 steps 1 and 4).
 //
-// Phase 1 (decode_split_kernel): one workgroup per (split of 64 pages, K/V head,
+// Phase 1 (decode_split_kernel): one workgroup per (split of 128 pages, K/V head,
 // sequence) serves up to HB query heads of that K/V head's group, so each K/V
-// page is read from HBM once for the whole group.  Its 4 waves take the split's
-// pages two at a time, round-robin.  In a wave, lane l holds tokens 2*(l/8) and
+// page is read from HBM once for the whole group.  The split index is the slow
+// grid dimension: workgroups are dealt round-robin to the 8 XCDs by linear id, so
+// each XCD gets an even share of (sequence, head) pairs at every split index
+// (with the split fastest, an XCD would only ever see splits j and j + 8, and
+// the early splits, active for every sequence, would pile onto a few XCDs).
+// The split's page ids are read once, one per lane, and taken from that
+// register wave-uniformly.  Its 4 waves take the split's pages two at a time,
+// round-robin.  In a wave, lane l holds tokens 2*(l/8) and
 // 2*(l/8)+1 of each page and the d columns {8*(l%8) + 64*c .. +8}; each (page,
 // head) block is 4 KB contiguous, so every 16-byte load instruction covers 8
 // whole 128-byte row segments.  The next page pair is fetched while the current
@@ -45,10 +51,10 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
   __shared__ float sm_lr[kDecWaves][HB];
   __shared__ float sm_acc[kDecWaves][HB][D];
 
-  const int split = blockIdx.x;
-  const int g = blockIdx.y / nhb;
-  const int hb = blockIdx.y % nhb;
-  const int s = blockIdx.z;
+  const int split = blockIdx.y;
+  const int hb = blockIdx.x % nhb;
+  const int g = (blockIdx.x / nhb) % Hkv;
+  const int s = blockIdx.x / (nhb * Hkv);
   const int G = Hq / Hkv;
   const int n = ctx[s];
   const int npages = (n + kPage - 1) / kPage;
@@ -57,8 +63,8 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
   const int p_end = min(npages, p_begin + kDecodePagesPerSplit);
 
   const int tid = threadIdx.x;
-  // wave index made provably wave-uniform, so page ids below are read with scalar
-  // loads (their waits do not drain the in-flight K/V vector loads)
+  // wave index made provably wave-uniform, so page indices derived from it stay in
+  // scalar registers (the page-id readlane below needs a uniform lane index)
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int tg = lane >> 3;  // token pair within the page
@@ -95,7 +101,23 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
     for (int i = 0; i < DL; ++i) acc[hh][i] = 0.f;
   }
 
+  // page ids of this split, lane i of register r holding page p_begin + 64 r + i;
+  // read back with readlane at a wave-uniform index
+  constexpr int kIdRegs = (kDecodePagesPerSplit + 63) / 64;
   const int32_t* trow = table + (size_t)s * max_pages;
+  int lane_pid[kIdRegs];
+#pragma unroll
+  for (int r = 0; r < kIdRegs; ++r) {
+    const int pg = p_begin + 64 * r + (tid & 63);
+    lane_pid[r] = pg < p_end ? trow[pg] : 0;
+  }
+  auto page_id = [&](int idx) {  // idx wave-uniform, 0 <= idx < kDecodePagesPerSplit
+    int id = __builtin_amdgcn_readlane(lane_pid[0], idx & 63);
+#pragma unroll
+    for (int r = 1; r < kIdRegs; ++r)
+      if ((idx >> 6) == r) id = __builtin_amdgcn_readlane(lane_pid[r], idx & 63);
+    return id;
+  };
   const size_t head_off = (size_t)g * kPage * D;
   const size_t page_stride = (size_t)Hkv * kPage * D;
 
@@ -112,7 +134,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
 #pragma unroll
     for (int pp = 0; pp < PP; ++pp) {
       const int p = min(p0 + pp, p_end - 1);
-      const size_t base = (size_t)trow[p] * page_stride + head_off;
+      const size_t base = (size_t)page_id(p - p_begin) * page_stride + head_off;
 #pragma unroll
       for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -308,7 +330,7 @@ template <int D, int HB>
 hipError_t launch_split(const DecodeArgs& a, float* ws_o, float* ws_l, int max_splits) {
   const int G = a.Hq / a.Hkv;
   const int nhb = (G + HB - 1) / HB;
-  const dim3 grid((unsigned)max_splits, (unsigned)(a.Hkv * nhb), (unsigned)a.S);
+  const dim3 grid((unsigned)(a.S * a.Hkv * nhb), (unsigned)max_splits);
   hipLaunchKernelGGL((decode_split_kernel<D, HB>), grid, dim3(kDecThreads), 0, (hipStream_t)a.stream,
                      (const uint16_t*)a.q, (const uint16_t*)a.kpages, (const uint16_t*)a.vpages, a.page_table,
                      a.ctx_lens, ws_o, ws_l, a.Hq, a.Hkv, a.max_pages, max_splits, nhb, a.scale * kLog2e);

@@ -36,7 +36,7 @@ struct DecodeArgs {
 
 // Pages handled by one split of the paged decode.  The workspace size depends on it.
 #ifndef FA_DECODE_PAGES_PER_SPLIT
-#define FA_DECODE_PAGES_PER_SPLIT 64
+#define FA_DECODE_PAGES_PER_SPLIT 128
 #endif
 constexpr int kDecodePagesPerSplit = FA_DECODE_PAGES_PER_SPLIT;
 

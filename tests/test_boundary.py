@@ -86,6 +86,7 @@ def test_decode_validation(L):
     assert dec(L, Hq=6, Hkv=4) == SHAPE
     assert dec(L, S=-1) == SHAPE
     assert dec(L, maxp=0) == SHAPE
+    assert dec(L, maxp=128 * 65535 + 1) == SHAPE   # more splits than one grid dimension holds
     assert dec(L, scale=float("-inf")) == SCALE
     assert dec(L, vp=MIS) == ALIGN
     assert dec(L, ws=Z) == WORKSPACE
@@ -96,9 +97,9 @@ def test_decode_validation(L):
 
 
 def test_workspace_size(L):
-    # one fp32 partial (d values + one logsumexp) per (sequence, head, split of 64 pages)
+    # one fp32 partial (d values + one logsumexp) per (sequence, head, split of 128 pages)
     for S, Hq, d, maxp in [(64, 32, 128, 1024), (1, 1, 64, 1), (3, 4, 64, 33)]:
-        splits = -(-maxp // 64)
+        splits = -(-maxp // 128)
         o_bytes = S * Hq * splits * d * 4
         assert fa.fa_decode_paged_workspace_size(S, Hq, d, maxp, 16) == -(-o_bytes // 256) * 256 + S * Hq * splits * 4
     assert fa.fa_decode_paged_workspace_size(1, 1, 96, 1, 16) == 0
