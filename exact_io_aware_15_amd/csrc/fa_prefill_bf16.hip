@@ -54,6 +54,7 @@ constexpr int kThreads = kWaves * 64;
 constexpr int kBR = kWaves * kRowsPerWave;  // 256 query rows per workgroup
 constexpr int kBC = 64;                     // keys per tile (two 32-key MFMA blocks)
 constexpr float kRescaleThreshold = 8.0f;   // log2 units: probabilities stay <= 256
+constexpr int kPrefetch = 4;                // LDS fragment reads kept ahead of the MFMAs
 #ifndef FA_PREFILL_STAGES
 #define FA_PREFILL_STAGES 2
 #endif
@@ -199,6 +200,14 @@ __device__ __forceinline__ void process_tile(WaveState<D>& st, const uint8_t* kb
       const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kb + (a * 32 + l32) * LY::ROWB + koff[kk]);
       sc[a] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, st.qf[kk], sc[a], 0, 0, 0);
     }
+  // schedule: kPrefetch fragment reads in flight ahead of the MFMA that consumes them
+  __builtin_amdgcn_sched_group_barrier(0x100, kPrefetch, 0);  // LDS reads
+#pragma unroll
+  for (int i = 0; i < 2 * KK - kPrefetch; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, kPrefetch, 0);
 
   // ---- online softmax
   const float mt = tile_rowmax<MASK>(sc, lim, c);
@@ -225,6 +234,14 @@ __device__ __forceinline__ void process_tile(WaveState<D>& st, const uint8_t* kb
         st.oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, cat), pb[a][h2],
                                                               st.oacc[db], 0, 0, 0);
       }
+  // same schedule for the V fragments (two transposing reads per MFMA)
+  __builtin_amdgcn_sched_group_barrier(0x100, 2 * kPrefetch, 1);
+#pragma unroll
+  for (int i = 0; i < 4 * DB - kPrefetch; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, kPrefetch, 1);
 }
 
 // HBM -> LDS copy of one K/V tile into buffer buf: this wave's 1 KB blocks
