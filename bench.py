@@ -11,7 +11,7 @@ against the MI355X peaks (bf16 dense MFMA 2516.6 TFLOP/s = 256 CU x 2.4 GHz x 40
 flop/clk; HBM3E 8000 GB/s).  `cpu_baseline` times the fp64 CPU oracle on a bounded
 sample of the same workload.
 
-Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--no-cpu-baseline]
+Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 30] [--no-cpu-baseline]
 """
 
 from __future__ import annotations
@@ -80,7 +80,7 @@ def decode_bytes(x, cfg):
 
 
 def cpu_baseline_prefill(x, cfg, stride):
-    """fp64 oracle on every `stride`-th query row of every head (bounded sample)."""
+    """fp64 oracle on every `stride`-th query row of every head (stride 1: the whole workload)."""
     import numpy as np
     import threadpoolctl
 
@@ -95,7 +95,8 @@ def cpu_baseline_prefill(x, cfg, stride):
     flops = 4.0 * cfg.d * float(vis.sum()) * cfg.B * cfg.Hq
     threads = max(i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()) or 1
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"every {stride}th query row ({len(rows)} rows) of all {cfg.B * cfg.Hq} heads of {cfg.name}; "
+            "sample": (f"all {cfg.N} query rows" if stride == 1 else f"every {stride}th query row ({len(rows)} rows)")
+                      + f" of all {cfg.B * cfg.Hq} heads of {cfg.name}; "
                       f"{dt:.1f} s of fp64 numpy",
             "seconds": round(dt, 2)}
 
@@ -126,9 +127,13 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=30,
+                    help="untimed steps first (the GPU clock takes tens of milliseconds of load to settle)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-row-stride", type=int, default=4)
+    ap.add_argument("--cpu-row-stride", type=int, default=1,
+                    help="oracle baseline on every n-th query row of the prefill (1 = the whole workload)")
+    ap.add_argument("--cpu-decode-seqs", type=int, default=64,
+                    help="oracle baseline on the first n sequences of the decode (64 = the whole workload)")
     ap.add_argument("--only", choices=["prefill", "decode"], default=None,
                     help="time one half of the step only (for profiling runs)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -249,7 +254,7 @@ def main():
         if run_p:
             res["cpu_baseline"] = cpu_baseline_prefill(px, pcfg, args.cpu_row_stride)
         if run_d:
-            cb = cpu_baseline_decode(dx, dcfg, 32)
+            cb = cpu_baseline_decode(dx, dcfg, min(args.cpu_decode_seqs, dcfg.num_seqs))
             if run_p:
                 res["decode"]["cpu_baseline"] = cb
             else:
