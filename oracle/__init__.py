@@ -12,8 +12,9 @@ Pages cited (by title and section):
   * screna.ai interview notes, FlashAttention block (S = QK^T, P = softmax(S))
     and MHA/MQA/GQA block (heads grouped, each group shares one K and V).
 
-Every function is "pinned" by the CPU tests in tests/test_oracle.py (closed forms,
-brute force on tiny shapes, identities).  Nothing here is "parity unpinned".
+Every function is "pinned" by the CPU tests in tests/test_oracle.py and
+tests/test_oracle_bwd.py (closed forms, brute force on tiny shapes, finite
+differences, identities).  Nothing here is "parity unpinned".
 """
 
 from .attention import (  # noqa: F401
@@ -23,3 +24,4 @@ from .attention import (  # noqa: F401
     lse_merge_ref,
     gather_pages_ref,
 )
+from .backward import attention_bwd_ref, attention_bwd_delta_ref  # noqa: F401
