@@ -1,4 +1,4 @@
-"""Exact attention (FlashAttention forward) and paged-KV decode for MI355X (gfx950).
+"""Exact attention (FlashAttention forward and backward) and paged-KV decode for MI355X (gfx950).
 
 Thin ctypes binding over libfa.so, whose C ABI is declared in include/fa.h.  The
 functions below carry the C names and only marshal arguments: they check dtypes,
@@ -21,6 +21,8 @@ __all__ = [
     "lib",
     "fa_fwd",
     "fa_fwd_f32",
+    "fa_bwd",
+    "fa_bwd_workspace_size",
     "fa_decode_paged",
     "fa_decode_paged_workspace_size",
     "fa_status_string",
@@ -52,6 +54,10 @@ def lib() -> ctypes.CDLL:
     L.fa_fwd.restype = i
     L.fa_fwd_f32.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp]
     L.fa_fwd_f32.restype = i
+    L.fa_bwd_workspace_size.argtypes = [i, i, i, i, i]
+    L.fa_bwd_workspace_size.restype = sz
+    L.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp, sz, vp]
+    L.fa_bwd.restype = i
     L.fa_decode_paged_workspace_size.argtypes = [i, i, i, i, i]
     L.fa_decode_paged_workspace_size.restype = sz
     L.fa_decode_paged.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp, sz, vp]
@@ -119,6 +125,44 @@ def fa_fwd(q, k, v, causal=False, scale=None, out=None, lse=None):
 def fa_fwd_f32(q, k, v, causal=False, scale=None, out=None, lse=None):
     """fp32 forward, same layouts as fa_fwd."""
     return _fwd("fa_fwd_f32", torch.float32, q, k, v, causal, scale, out, lse)
+
+
+def fa_bwd_workspace_size(B, Hq, Hkv, N, d) -> int:
+    return int(lib().fa_bwd_workspace_size(B, Hq, Hkv, N, d))
+
+
+def fa_bwd(q, k, v, o, lse, dout, causal=False, scale=None, dq=None, dk=None, dv=None, workspace=None):
+    """bf16 backward: q, o, dout [B,Hq,N,d]; k, v [B,Hkv,N,d]; lse fp32 [B,Hq,N] (from fa_fwd)
+    -> (dQ [B,Hq,N,d], dK [B,Hkv,N,d], dV [B,Hkv,N,d]) in bf16."""
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q must be [B, Hq, N, d] and k, v [B, Hkv, N, d]")
+    B, Hq, N, d = q.shape
+    Hkv = k.shape[1]
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on a GPU")
+    bf = torch.bfloat16
+    for t, n, shp in ((q, "q", (B, Hq, N, d)), (k, "k", (B, Hkv, N, d)), (v, "v", (B, Hkv, N, d)),
+                      (o, "o", (B, Hq, N, d)), (dout, "dout", (B, Hq, N, d))):
+        _need(t, n, bf, shp, dev)
+    _need(lse, "lse", torch.float32, (B, Hq, N), dev)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dq = torch.empty((B, Hq, N, d), dtype=bf, device=dev) if dq is None else dq
+    dk = torch.empty((B, Hkv, N, d), dtype=bf, device=dev) if dk is None else dk
+    dv = torch.empty((B, Hkv, N, d), dtype=bf, device=dev) if dv is None else dv
+    _need(dq, "dq", bf, (B, Hq, N, d), dev)
+    _need(dk, "dk", bf, (B, Hkv, N, d), dev)
+    _need(dv, "dv", bf, (B, Hkv, N, d), dev)
+    need = fa_bwd_workspace_size(B, Hq, Hkv, N, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    st = lib().fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
+                      B, Hq, Hkv, N, d, int(bool(causal)), float(scale), _ptr(workspace),
+                      workspace.numel() * workspace.element_size(), _stream(q))
+    if st != FA_OK:
+        raise FAError(st, "fa_bwd")
+    return dq, dk, dv
 
 
 def fa_decode_paged_workspace_size(num_seqs, Hq, d, max_pages_per_seq, page_size=16) -> int:

@@ -19,7 +19,7 @@ CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libfa.so")
 BUILD_DIR = os.path.join(PKG, "_build")
 
-SOURCES = ["fa_api.cpp", "fa_prefill_bf16.hip", "fa_prefill_f32.hip", "fa_decode.hip"]
+SOURCES = ["fa_api.cpp", "fa_prefill_bf16.hip", "fa_prefill_f32.hip", "fa_decode.hip", "fa_backward.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

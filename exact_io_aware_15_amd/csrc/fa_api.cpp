@@ -69,6 +69,26 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
   return finish(fa::launch_fwd_bf16(a), stream);
 }
 
+size_t fa_bwd_workspace_size(int B, int Hq, int Hkv, int N, int d) {
+  if (B < 0 || N < 0 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || (d != 64 && d != 128)) return 0;
+  return fa::bwd_plan(B, Hq, Hkv, N, d).bytes;
+}
+
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout, void* dq,
+           void* dk, void* dv, int B, int Hq, int Hkv, int N, int d, int causal, float scale, void* workspace,
+           size_t workspace_bytes, void* stream) {
+  bool empty = false;
+  int st = check_fwd(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, scale, &empty);
+  if (st != FA_OK || empty) return st;
+  if (!dout || !dq || !dk || !dv) return FA_ERR_NULL;
+  if (!aligned16(dout) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv)) return FA_ERR_ALIGN;
+  const fa::BwdPlan pl = fa::bwd_plan(B, Hq, Hkv, N, d);
+  if (!workspace || workspace_bytes < pl.bytes) return FA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return FA_ERR_ALIGN;
+  fa::BwdArgs a{q, k, v, o, lse, dout, dq, dk, dv, B, Hq, Hkv, N, d, causal != 0, scale, workspace, stream};
+  return finish(fa::launch_bwd_bf16(a), stream);
+}
+
 int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B, int Hq, int Hkv,
                int N, int d, int causal, float scale, void* stream) {
   bool empty = false;

@@ -1,0 +1,552 @@
+// Exact-attention backward on gfx950 matrix cores: dQ, dK, dV from Q, K, V, the
+// forward's O and per-row logsumexp L, and the upstream gradient dO.
+//
+// "Phase 08 -- Inference Optimization at Depth", Concepts list (the FlashAttention
+// backward needs only O and L, never the N x N matrix) and Lab 01 step 6 (the
+// optional backward pass).  The pages give no formulas; the kernels evaluate the
+// standard chain rule through the softmax, recomputing P tile by tile from Q, K
+// and the stored L instead of reading it:
+//
+//   D   = rowsum(dO * O)                     (bwd_delta_kernel)
+//   P   = exp(scale * Q K^T - L)             (masked entries 0)
+//   dP  = dO V^T,   dS = P * (dP - D)
+//   dQ  = scale * dS K                       (bwd_dq_kernel: one pass over K/V per query block)
+//   dV  = P^T dO,   dK = scale * dS^T Q      (bwd_dkdv_kernel: one pass over Q/dO per key block)
+//
+// Both main kernels run one 64-lane wave per SIMD (four per workgroup, 512
+// registers each) and stream the other operand in 64-row tiles through two LDS
+// buffers, copied HBM -> LDS with the LDS-destination bit of 128-bit buffer loads
+// (rows past N read as zero), rows unpadded with XOR-swizzled 16-byte chunks.
+// Every product runs on v_mfma_f32_32x32x16_bf16 with fp32 accumulation.  The dQ
+// kernel computes S^T and dP^T with a lane per query row (so the row's L and D sit
+// in one register), like the forward, and accumulates dQ^T = K^T dS^T reading K^T
+// fragments with ds_read_b64_tr_b16.  The dK/dV kernel computes S and dP with a lane
+// per key and accumulates dV = P^T dO and dK = dS^T Q reading dO and Q through the
+// transposing reads.  Grouped query heads: a K/V head's gradients sum over the query
+// heads of its group; when there are too few (key block, K/V head) pairs to fill
+// the GPU (multi-query), the group's heads are split into chunks whose fp32 partial
+// sums a last kernel adds up.
+#include "fa_device.h"
+#include "fa_launch.h"
+
+namespace fa {
+namespace {
+
+constexpr int kBwdWaves = 4;                 // one wave per SIMD
+constexpr int kBwdThreads = kBwdWaves * 64;
+constexpr int kWaveRows = 32;                // query rows (dQ) or keys (dK/dV) per wave
+constexpr int kBlockRows = kBwdWaves * kWaveRows;  // 128 per workgroup
+constexpr int kTile = 64;                    // rows of the streamed operand per tile
+
+template <int D>
+struct BLay {
+  static constexpr int ROWB = D * 2;              // bytes per row
+  static constexpr int CPR = ROWB / 16;           // 16-byte chunks per row
+  static constexpr int RPB = 1024 / ROWB;         // rows per 1 KB block
+  static constexpr int TBYTES = kTile * ROWB;     // one tile
+  static constexpr int BPW = TBYTES / 1024 / kBwdWaves;  // 1 KB blocks copied per wave
+  static_assert(BPW * kBwdWaves * 1024 == TBYTES, "tile copy must split evenly over the waves");
+  // physical chunk = logical chunk ^ swz(row); depends on row & 15 only
+  __host__ __device__ static constexpr int swz(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
+};
+
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+
+// HBM -> LDS copy of tile rows r0 .. r0+63 of one (batch, head) slice: this wave's
+// 1 KB blocks w, w + 4, ...  Block w + 4i lies 4 KB after block w in both HBM and
+// LDS and the swizzle repeats with that period, so one per-lane offset cp serves all.
+template <int D>
+__device__ __forceinline__ void copy_tile(uint8_t* dst, const void* base, uint32_t bytes, uint32_t cp, int r0, int w) {
+  using L = BLay<D>;
+  constexpr uint32_t kStride = kBwdWaves * 1024;
+  static_assert((kStride / L::ROWB) % 16 == 0, "swizzle must repeat every kBwdWaves blocks");
+  const auto rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+  const uint32_t off = (uint32_t)r0 * L::ROWB + cp;
+#pragma unroll
+  for (int i = 0; i < L::BPW; ++i)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (FA_LDS void*)(dst + w * 1024 + i * kStride), 16, off, i * kStride,
+                                             0, 0);
+}
+
+// 64 fp32 row values (L or D) of rows r0 .. r0+63 into dst; lanes 0..15 of the
+// calling wave, rows past N read as zero.
+__device__ __forceinline__ void copy_rowvals(float* dst, const float* base, int N, int r0, int lane) {
+  if (lane < 16) {
+    const auto rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), (short)0, (uint32_t)N * 4, 0x00020000);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (FA_LDS void*)dst, 16, (uint32_t)r0 * 4 + lane * 16, 0, 0, 0);
+  }
+}
+
+// Lane's byte offset for copying block w of a tile (row w*RPB + lane/CPR, swizzled chunk).
+template <int D>
+__device__ __forceinline__ uint32_t copy_offset(int w, int lane) {
+  using L = BLay<D>;
+  const int r = w * L::RPB + lane / L::CPR;
+  return r * L::ROWB + (((lane % L::CPR) ^ L::swz(r)) << 4);
+}
+
+// Offsets of the transposing fragment reads X^T[d][rows] from a row-major tile:
+// for d block db, the lower (rows R0 + 4hi + 0..3) and upper (R0 + 8 + 4hi + 0..3)
+// reads of a 16-row group R0 (R0 a multiple of 16).  Source lane li of 16-lane
+// group grp reads row 4hi + li/4 (+8) and d = 32db + 16(grp&1) + 4(li&3) .. +3.
+template <int D>
+__device__ __forceinline__ void tr_offsets(int lane, int (&tlo)[D / 32], int (&thi)[D / 32]) {
+  using L = BLay<D>;
+  const int hi = lane >> 5, grp = lane >> 4, li = lane & 15;
+  const int vr = 4 * hi + (li >> 2);
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) {
+    const int lc = 4 * db + 2 * (grp & 1) + ((li & 3) >> 1);
+    tlo[db] = vr * L::ROWB + ((lc ^ L::swz(vr)) << 4) + (li & 1) * 8;
+    thi[db] = (vr + 8) * L::ROWB + ((lc ^ L::swz(vr + 8)) << 4) + (li & 1) * 8;
+  }
+}
+
+__device__ __forceinline__ bf16x8 tr_frag(const uint8_t* base, int lo, int up) {
+  const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS s16x4*)(base + lo));
+  const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS s16x4*)(base + up));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+__device__ __forceinline__ u32x4 ld16(const uint16_t* p) { return *reinterpret_cast<const u32x4*>(p); }
+
+// ---------------------------------------------------------------------------
+// D = rowsum(dO * O): D/8 lanes per row, 16-byte loads, DPP reduction.
+template <int D>
+__global__ __launch_bounds__(256) void bwd_delta_kernel(const uint16_t* __restrict__ O, const uint16_t* __restrict__ dO,
+                                                        float* __restrict__ Dlt, long long rows) {
+  constexpr int LPR = D / 8;  // lanes per row: 16 (d128) or 8 (d64)
+  const long long gid = (long long)blockIdx.x * 256 + threadIdx.x;
+  const long long row = gid / LPR;
+  const int c = (int)(gid % LPR);
+  float acc = 0.f;
+  if (row < rows) {
+    const u32x4 o = ld16(O + row * D + c * 8);
+    const u32x4 g = ld16(dO + row * D + c * 8);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      acc = __builtin_fmaf(bf16lo_to_f32(o[e]), bf16lo_to_f32(g[e]), acc);
+      acc = __builtin_fmaf(bf16hi_to_f32(o[e]), bf16hi_to_f32(g[e]), acc);
+    }
+  }
+  acc = sum8(acc);                         // lanes l ^ 1, 2, 4
+  if (LPR == 16) acc += dpp<0x128>(acc);   // and l ^ 8 (row_ror:8 inside 16-lane rows)
+  if (row < rows && c == 0) Dlt[row] = acc;
+}
+
+// ---------------------------------------------------------------------------
+// dQ: one workgroup per (128-row query block, query head, batch), four waves of 32
+// rows.  K and V tiles of 64 keys stream through LDS (two buffers each).
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+    const uint16_t* __restrict__ dO, const float* __restrict__ Lse, const float* __restrict__ Dlt,
+    uint16_t* __restrict__ dQ, int B, int Hq, int Hkv, int N, float cs /* scale * log2 e */, float scale) {
+  using L = BLay<D>;
+  constexpr int KK = D / 16, DB = D / 32;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[4 * L::TBYTES];  // K[2], V[2]
+
+  const int nqb = (N + kBlockRows - 1) / kBlockRows;
+  const int BH = B * Hq;
+  const int qb = CAUSAL ? (nqb - 1 - (int)(blockIdx.x / BH)) : (int)(blockIdx.x / BH);  // heaviest first
+  const int bh = blockIdx.x % BH;
+  const int b = bh / Hq, h = bh % Hq;
+  const int g = h / (Hq / Hkv);
+
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
+  const int rw0 = qb * kBlockRows + w * kWaveRows;
+  const int qrow = rw0 + l32;
+  const bool row_ok = qrow < N;
+
+  const size_t qoff = (size_t)(b * Hq + h) * N;
+  const uint16_t* kbase = K + (size_t)(b * Hkv + g) * N * D;
+  const uint16_t* vbase = V + (size_t)(b * Hkv + g) * N * D;
+  const uint32_t head_bytes = (uint32_t)N * D * 2;
+
+  // Q and dO rows as B operands (Q^T, dO^T fragments): row qrow, d = kk*16 + hi*8 .. +8
+  bf16x8 qf[KK], gf[KK];
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk) {
+    u32x4 x = {0u, 0u, 0u, 0u}, y = {0u, 0u, 0u, 0u};
+    if (row_ok) {
+      x = ld16(Q + (qoff + qrow) * D + kk * 16 + hi * 8);
+      y = ld16(dO + (qoff + qrow) * D + kk * 16 + hi * 8);
+    }
+    qf[kk] = __builtin_bit_cast(bf16x8, x);
+    gf[kk] = __builtin_bit_cast(bf16x8, y);
+  }
+  // the row's statistics: P = exp2(cs * s - l2); rows past N get P = 0
+  const float l2 = row_ok ? Lse[qoff + qrow] * kLog2e : INFINITY;
+  const float dl = row_ok ? Dlt[qoff + qrow] : 0.f;
+
+  f32x16 acc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
+
+  int roff[KK];
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk) roff[kk] = l32 * L::ROWB + (((2 * kk + hi) ^ L::swz(l32)) << 4);
+  int tlo[DB], thi[DB];
+  tr_offsets<D>(lane, tlo, thi);
+  const uint32_t cp = copy_offset<D>(w, lane);
+
+  const int kend = CAUSAL ? min(N, (qb + 1) * kBlockRows) : N;
+  const int ntiles = (kend + kTile - 1) / kTile;
+
+  if (ntiles > 0) {
+    copy_tile<D>(smem, kbase, head_bytes, cp, 0, w);
+    copy_tile<D>(smem + 2 * L::TBYTES, vbase, head_bytes, cp, 0, w);
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  __syncthreads();
+
+  for (int t0 = 0; t0 < ntiles; t0 += 2) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int t = t0 + u;
+      if (t >= ntiles) break;
+      const int j0 = t * kTile;
+      if (t + 1 < ntiles) {
+        copy_tile<D>(smem + (1 - u) * L::TBYTES, kbase, head_bytes, cp, j0 + kTile, w);
+        copy_tile<D>(smem + (3 - u) * L::TBYTES, vbase, head_bytes, cp, j0 + kTile, w);
+      }
+      const bool skip = CAUSAL && (j0 > rw0 + kWaveRows - 1);
+      if (!skip) {
+        const uint8_t* kb = smem + u * L::TBYTES;
+        const uint8_t* vb = smem + (2 + u) * L::TBYTES;
+        // S^T = K Q^T and dP^T = V dO^T; lane holds keys a*32 + 8(r/4) + 4hi + r%4 of its row
+        f32x16 s[2], dp[2];
+#pragma unroll
+        for (int a = 0; a < 2; ++a)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            s[a][r] = 0.f;
+            dp[a][r] = 0.f;
+          }
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk)
+#pragma unroll
+          for (int a = 0; a < 2; ++a) {
+            const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kb + a * 32 * L::ROWB + roff[kk]);
+            s[a] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], s[a], 0, 0, 0);
+          }
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk)
+#pragma unroll
+          for (int a = 0; a < 2; ++a) {
+            const bf16x8 vf = *reinterpret_cast<const bf16x8*>(vb + a * 32 * L::ROWB + roff[kk]);
+            dp[a] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, gf[kk], dp[a], 0, 0, 0);
+          }
+        // dS^T = P^T * (dP^T - D), masked keys (after the row, or past N) give 0
+        const bool need_mask = CAUSAL ? (j0 + kTile - 1 > rw0) : (j0 + kTile > N);
+        const int lim = (CAUSAL ? qrow - j0 : N - 1 - j0) - 4 * hi;
+        bf16x8 dsb[2][2];
+#pragma unroll
+        for (int a = 0; a < 2; ++a)
+#pragma unroll
+          for (int h2 = 0; h2 < 2; ++h2) {
+            u32x4 pk;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              float d2[2];
+#pragma unroll
+              for (int e = 0; e < 2; ++e) {
+                const int r = h2 * 8 + 2 * j + e;
+                float p = exp2_fast(__builtin_fmaf(s[a][r], cs, -l2));
+                if (need_mask && a * 32 + 8 * (r >> 2) + (r & 3) > lim) p = 0.f;
+                d2[e] = p * (dp[a][r] - dl);
+              }
+              pk[j] = pack_bf16x2(d2[0], d2[1]);
+            }
+            dsb[a][h2] = __builtin_bit_cast(bf16x8, pk);
+          }
+        // dQ^T += K^T dS^T
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int a = 0; a < 2; ++a)
+#pragma unroll
+          for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+              const uint8_t* grp0 = kb + (a * 32 + h2 * 16) * L::ROWB;
+              acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag(grp0, tlo[db], thi[db]), dsb[a][h2], acc[db],
+                                                                0, 0, 0);
+            }
+      }
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): tile t+1 has landed
+      __syncthreads();
+    }
+  }
+
+  // dQ = scale * (dQ^T)^T: lane holds d = db*32 + 8*g4 + 4*hi + 0..3 of its row
+  if (row_ok) {
+    uint16_t* out = dQ + (qoff + qrow) * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        u32x2 w2;
+        w2[0] = pack_bf16x2(acc[db][4 * g4 + 0] * scale, acc[db][4 * g4 + 1] * scale);
+        w2[1] = pack_bf16x2(acc[db][4 * g4 + 2] * scale, acc[db][4 * g4 + 3] * scale);
+        *reinterpret_cast<u32x2*>(out + db * 32 + 8 * g4 + 4 * hi) = w2;
+      }
+  }
+}
+
+// Source of the dK/dV kernel's streamed items: item i is row tile
+// t_first + i % per_head of query head h_begin + i / per_head.
+struct ItemSrc {
+  const uint16_t* Q;
+  const uint16_t* dO;
+  const float* Lse;
+  const float* Dlt;
+  int b, Hq, N, h_begin, per_head, t_first;
+  uint32_t head_bytes, cp;
+  int w, lane;
+};
+
+// Start the HBM -> LDS copies of one item into buffer buf: its Q and dO tiles
+// (all waves) and the 64 rows' L (wave 0) and D (wave 1).
+template <int D>
+__device__ __forceinline__ void issue_item(const ItemSrc& s, uint8_t* smem, float (*rowv)[2][kTile], int item,
+                                           int buf) {
+  using L = BLay<D>;
+  const int h = s.h_begin + item / s.per_head;
+  const int r0 = (s.t_first + item % s.per_head) * kTile;
+  const size_t qo = (size_t)(s.b * s.Hq + h) * s.N;
+  copy_tile<D>(smem + buf * L::TBYTES, s.Q + qo * D, s.head_bytes, s.cp, r0, s.w);
+  copy_tile<D>(smem + (2 + buf) * L::TBYTES, s.dO + qo * D, s.head_bytes, s.cp, r0, s.w);
+  if (s.w == 0) copy_rowvals(rowv[buf][0], s.Lse + qo, s.N, r0, s.lane);
+  if (s.w == 1) copy_rowvals(rowv[buf][1], s.Dlt + qo, s.N, r0, s.lane);
+}
+
+// ---------------------------------------------------------------------------
+// dK, dV: one workgroup per (128-key block, K/V head, batch, chunk of the group's
+// query heads), four waves of 32 keys.  For every query head of the chunk, Q and
+// dO tiles of 64 rows (and the rows' L and D) stream through LDS (two buffers).
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+    const uint16_t* __restrict__ dO, const float* __restrict__ Lse, const float* __restrict__ Dlt,
+    uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, float* __restrict__ partK, float* __restrict__ partV,
+    int B, int Hq, int Hkv, int N, int heads_per_chunk, int nchunks, float cs, float scale) {
+  using L = BLay<D>;
+  constexpr int KK = D / 16, DB = D / 32;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[4 * L::TBYTES];  // Q[2], dO[2]
+  __shared__ __attribute__((aligned(16))) float rowv[2][2][kTile];      // [buffer][L, D][row]
+
+  const int G = Hq / Hkv;
+  const int per_kb = B * Hkv * nchunks;
+  const int kb = blockIdx.x / per_kb;  // key blocks in order: the first have the most rows (causal)
+  const int rem = blockIdx.x % per_kb;
+  const int chunk = rem % nchunks;
+  const int bg = rem / nchunks;
+  const int b = bg / Hkv, g = bg % Hkv;
+  const int h_begin = g * G + chunk * heads_per_chunk;
+  const int nh = min(heads_per_chunk, (g + 1) * G - h_begin);
+
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
+  const int kw0 = kb * kBlockRows + w * kWaveRows;  // this wave's first key
+  const int key = kw0 + l32;
+
+  const size_t kvoff = (size_t)(b * Hkv + g) * N;
+  // K and V rows as B operands (K^T, V^T fragments): key, d = kk*16 + hi*8 .. +8
+  bf16x8 kf[KK], vf[KK];
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk) {
+    u32x4 x = {0u, 0u, 0u, 0u}, y = {0u, 0u, 0u, 0u};
+    if (key < N) {
+      x = ld16(K + (kvoff + key) * D + kk * 16 + hi * 8);
+      y = ld16(V + (kvoff + key) * D + kk * 16 + hi * 8);
+    }
+    kf[kk] = __builtin_bit_cast(bf16x8, x);
+    vf[kk] = __builtin_bit_cast(bf16x8, y);
+  }
+  f32x16 dka[DB], dva[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      dka[db][r] = 0.f;
+      dva[db][r] = 0.f;
+    }
+
+  int roff[KK];
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk) roff[kk] = l32 * L::ROWB + (((2 * kk + hi) ^ L::swz(l32)) << 4);
+  int tlo[DB], thi[DB];
+  tr_offsets<D>(lane, tlo, thi);
+  const uint32_t cp = copy_offset<D>(w, lane);
+  const uint32_t head_bytes = (uint32_t)N * D * 2;
+
+  // (head, row tile) items in order; causal: rows before the block's first key are skipped
+  const int nt = (N + kTile - 1) / kTile;
+  const int t_first = CAUSAL ? (kb * kBlockRows) / kTile : 0;
+  const int per_head = nt - t_first;
+  const int total = nh * per_head;
+
+  const ItemSrc src{Q, dO, Lse, Dlt, b, Hq, N, h_begin, per_head, t_first, head_bytes, cp, w, lane};
+  if (total > 0) issue_item<D>(src, smem, rowv, 0, 0);
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  __syncthreads();
+
+  for (int i0 = 0; i0 < total; i0 += 2) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int item = i0 + u;
+      if (item >= total) break;
+      if (item + 1 < total) issue_item<D>(src, smem, rowv, item + 1, 1 - u);
+      const int r0 = (t_first + item % per_head) * kTile;
+      // causal: a tile whose last row precedes the wave's first key adds nothing
+      const bool skip = CAUSAL && (r0 + kTile - 1 < kw0);
+      if (!skip) {
+        const uint8_t* qb_ = smem + u * L::TBYTES;
+        const uint8_t* gb_ = smem + (2 + u) * L::TBYTES;
+        const bool need_mask = (CAUSAL && r0 < kw0 + kWaveRows - 1) || (r0 + kTile > N);
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+          // S = Q K^T and dP = dO V^T for rows rb*32 + 8(r/4) + 4hi + r%4 of the tile
+          f32x16 s, dp;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            s[r] = 0.f;
+            dp[r] = 0.f;
+          }
+#pragma unroll
+          for (int kk = 0; kk < KK; ++kk) {
+            const bf16x8 qa = *reinterpret_cast<const bf16x8*>(qb_ + rb * 32 * L::ROWB + roff[kk]);
+            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[kk], s, 0, 0, 0);
+          }
+#pragma unroll
+          for (int kk = 0; kk < KK; ++kk) {
+            const bf16x8 ga = *reinterpret_cast<const bf16x8*>(gb_ + rb * 32 * L::ROWB + roff[kk]);
+            dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga, vf[kk], dp, 0, 0, 0);
+          }
+          // P and dS for the lane's key and 16 rows; row values from LDS, 4 rows per read
+          bf16x8 pb[2], dsb[2];
+#pragma unroll
+          for (int s2 = 0; s2 < 2; ++s2) {
+            u32x4 pk, dk;
+#pragma unroll
+            for (int q4 = 0; q4 < 2; ++q4) {
+              const int rr = rb * 32 + 16 * s2 + 8 * q4 + 4 * hi;  // first of 4 consecutive rows
+              const f32x4 lv = *reinterpret_cast<const f32x4*>(&rowv[u][0][rr]);
+              const f32x4 dv = *reinterpret_cast<const f32x4*>(&rowv[u][1][rr]);
+              float pv[4], dsv[4];
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                const int r = 8 * s2 + 4 * q4 + i;  // accumulator index of row rr + i
+                float p = exp2_fast(__builtin_fmaf(s[r], cs, -lv[i] * kLog2e));
+                const int row = r0 + rr + i;
+                if (need_mask && ((CAUSAL && key > row) || row >= N)) p = 0.f;
+                pv[i] = p;
+                dsv[i] = p * (dp[r] - dv[i]);
+              }
+              pk[2 * q4] = pack_bf16x2(pv[0], pv[1]);
+              pk[2 * q4 + 1] = pack_bf16x2(pv[2], pv[3]);
+              dk[2 * q4] = pack_bf16x2(dsv[0], dsv[1]);
+              dk[2 * q4 + 1] = pack_bf16x2(dsv[2], dsv[3]);
+            }
+            pb[s2] = __builtin_bit_cast(bf16x8, pk);
+            dsb[s2] = __builtin_bit_cast(bf16x8, dk);
+          }
+          // dV += P^T dO, dK += dS^T Q over the 32 rows (two 16-row steps)
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+              const int r0g = (rb * 32 + 16 * s2) * L::ROWB;
+              dva[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pb[s2], tr_frag(gb_ + r0g, tlo[db], thi[db]), dva[db],
+                                                                0, 0, 0);
+              dka[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dsb[s2], tr_frag(qb_ + r0g, tlo[db], thi[db]), dka[db],
+                                                                0, 0, 0);
+            }
+        }
+      }
+      __builtin_amdgcn_s_waitcnt(0x0F70);
+      __syncthreads();
+    }
+  }
+
+  // lane holds keys kw0 + 8(r/4) + 4hi + r%4 at d = db*32 + l32
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int kr = kw0 + 8 * (r >> 2) + 4 * hi + (r & 3);
+    if (kr >= N) continue;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const size_t idx = (kvoff + kr) * D + db * 32 + l32;
+      if (nchunks == 1) {
+        dK[idx] = __builtin_bit_cast(uint16_t, to_bf16(dka[db][r] * scale));
+        dV[idx] = __builtin_bit_cast(uint16_t, to_bf16(dva[db][r]));
+      } else {
+        const size_t pidx = (size_t)chunk * B * Hkv * N * D + idx;
+        partK[pidx] = dka[db][r] * scale;
+        partV[pidx] = dva[db][r];
+      }
+    }
+  }
+}
+
+// Sum of the head-chunk partials of dK and dV, rounded to bf16.
+__global__ __launch_bounds__(256) void bwd_reduce_kernel(const float* __restrict__ partK, const float* __restrict__ partV,
+                                                         uint16_t* __restrict__ dK, uint16_t* __restrict__ dV,
+                                                         long long n, int nchunks) {
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  float sk = 0.f, sv = 0.f;
+  for (int c = 0; c < nchunks; ++c) {
+    sk += partK[(size_t)c * n + i];
+    sv += partV[(size_t)c * n + i];
+  }
+  dK[i] = __builtin_bit_cast(uint16_t, to_bf16(sk));
+  dV[i] = __builtin_bit_cast(uint16_t, to_bf16(sv));
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch_bwd_t(const BwdArgs& a) {
+  hipStream_t st = (hipStream_t)a.stream;
+  const BwdPlan pl = bwd_plan(a.B, a.Hq, a.Hkv, a.N, a.d);
+  float* dlt = (float*)a.workspace;
+  float* partK = (float*)((uint8_t*)a.workspace + pl.part_offset);
+  float* partV = partK + pl.part_elems;
+  const long long rows = (long long)a.B * a.Hq * a.N;
+  constexpr int LPR = D / 8;
+  hipLaunchKernelGGL((bwd_delta_kernel<D>), dim3((unsigned)((rows * LPR + 255) / 256)), dim3(256), 0, st,
+                     (const uint16_t*)a.o, (const uint16_t*)a.dout, dlt, rows);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const float cs = a.scale * kLog2e;
+  const int nqb = (a.N + kBlockRows - 1) / kBlockRows;
+  hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)(nqb * a.B * a.Hq)), dim3(kBwdThreads), 0, st,
+                     (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (const uint16_t*)a.dout, a.lse,
+                     dlt, (uint16_t*)a.dq, a.B, a.Hq, a.Hkv, a.N, cs, a.scale);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)(nqb * a.B * a.Hkv * pl.nchunks)),
+                     dim3(kBwdThreads), 0, st, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
+                     (const uint16_t*)a.dout, a.lse, dlt, (uint16_t*)a.dk, (uint16_t*)a.dv, partK, partV, a.B, a.Hq,
+                     a.Hkv, a.N, pl.heads_per_chunk, pl.nchunks, cs, a.scale);
+  e = hipGetLastError();
+  if (e != hipSuccess || pl.nchunks == 1) return e;
+  const long long n = (long long)a.B * a.Hkv * a.N * D;
+  hipLaunchKernelGGL(bwd_reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, partK, partV,
+                     (uint16_t*)a.dk, (uint16_t*)a.dv, n, pl.nchunks);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_bwd_bf16(const BwdArgs& a) {
+  if (a.d == 64) return a.causal ? launch_bwd_t<64, true>(a) : launch_bwd_t<64, false>(a);
+  return a.causal ? launch_bwd_t<128, true>(a) : launch_bwd_t<128, false>(a);
+}
+
+}  // namespace fa

@@ -51,7 +51,50 @@ inline size_t decode_workspace_bytes(int S, int Hq, int d, int max_pages) {
   return ((o_bytes + 255) / 256) * 256 + l_bytes;
 }
 
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const float* lse;
+  const void* dout;
+  void* dq;
+  void* dk;
+  void* dv;
+  int B, Hq, Hkv, N, d;
+  bool causal;
+  float scale;
+  void* workspace;
+  void* stream;
+};
+
+// Backward launch plan.  dK/dV workgroups cover 128 keys of one K/V head; when
+// there are fewer than 512 of them, the query heads of each group are split into
+// chunks (each workgroup one chunk) whose fp32 partial sums are added at the end.
+// Workspace: D = rowsum(dO * O) [B][Hq][N] fp32 (padded to 256 B), then the dK and
+// dV partials [chunks][B][Hkv][N][d] fp32 each when chunks > 1.
+struct BwdPlan {
+  int nchunks, heads_per_chunk;
+  size_t part_offset, part_elems, bytes;
+};
+inline BwdPlan bwd_plan(int B, int Hq, int Hkv, int N, int d) {
+  BwdPlan p;
+  const long long nkb = (N + 127) / 128;
+  const long long base = (long long)B * Hkv * nkb;
+  const int G = Hq / Hkv;
+  int nch = 1;
+  if (base > 0 && base < 512) nch = (int)((512 + base - 1) / base);
+  if (nch > G) nch = G;
+  p.heads_per_chunk = (G + nch - 1) / nch;
+  p.nchunks = (G + p.heads_per_chunk - 1) / p.heads_per_chunk;
+  p.part_offset = (((size_t)B * Hq * N * sizeof(float)) + 255) / 256 * 256;
+  p.part_elems = p.nchunks > 1 ? (size_t)p.nchunks * B * Hkv * N * d : 0;
+  p.bytes = p.part_offset + 2 * p.part_elems * sizeof(float);
+  return p;
+}
+
 hipError_t launch_fwd_bf16(const FwdArgs& a);
+hipError_t launch_bwd_bf16(const BwdArgs& a);
 hipError_t launch_fwd_f32(const FwdArgs& a);
 hipError_t launch_decode_paged(const DecodeArgs& a);
 

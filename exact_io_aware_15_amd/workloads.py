@@ -121,6 +121,13 @@ def make_prefill(B, Hq, Hkv, N, d, dtype="bf16", seed=0, value_scale=1.0):
     return {"q": q, "k": k, "v": v}
 
 
+def make_grad_output(B, Hq, N, d, dtype="bf16", seed=0):
+    """Upstream gradient dO [B, Hq, N, d] for the backward: N(0,1) from its own
+    stream (seed + 7919, so it is independent of the forward inputs of the same seed)."""
+    rng = np.random.default_rng(seed + 7919)
+    return _to(_normal(rng, (B, Hq, N, d)), dtype)
+
+
 def make_decode(num_seqs, Hq, Hkv, d, ctx_lo=1, ctx_hi=64, seed=0, page_size=16,
                 max_pages_per_seq=None, fixed_ctx=(), dtype="bf16"):
     """Paged-KV decode inputs as CPU tensors.

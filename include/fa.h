@@ -83,6 +83,43 @@ int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* 
                void* stream);
 
 /*
+ * fa_bwd_workspace_size -- bytes of device workspace fa_bwd needs for these
+ * sizes: D = rowsum(dO * O) per row (fp32), plus fp32 partial sums of dK and dV
+ * when a K/V head's query heads are split over several workgroups (few K/V
+ * heads).  Returns 0 when an argument is out of range.
+ */
+size_t fa_bwd_workspace_size(int B, int Hq, int Hkv, int N, int d);
+
+/*
+ * fa_bwd -- bf16 exact-attention backward: the gradients of a loss with respect
+ * to q, k and v, given its gradient dout with respect to the forward's output.
+ *
+ * Pages: "Phase 08", Concepts (the FlashAttention backward keeps only O and the
+ * logsumexp L from the forward, not the N x N matrix) and Lab 01 step 6 (the
+ * optional backward).  The probabilities are recomputed tile by tile from q, k
+ * and lse; with S = scale * q k^T (masked as in fa_fwd), P = exp(S - L),
+ * D = rowsum(dout * o), dP = dout v^T and dS = P * (dP - D):
+ *   dq = scale * dS k,   dk = scale * dS^T q,   dv = P^T dout,
+ * dk and dv summed over the query heads that share a K/V head.
+ *
+ *   q, o, dout, dq [B, Hq, N, d] bf16;   k, v, dk, dv [B, Hkv, N, d] bf16
+ *   lse [B, Hq, N] fp32: the logsumexp fa_fwd returned for the same q, k, v,
+ *       causal and scale; o its output.
+ *   dq, dk, dv are written completely (out, fp32 accumulation rounded to
+ *   nearest even); they must not alias the inputs.
+ *   workspace: device memory of at least fa_bwd_workspace_size(B, Hq, Hkv, N, d)
+ *   bytes, 16-byte aligned, owned by the caller; contents on entry do not matter.
+ *   Calls sharing a workspace must be ordered (same stream).
+ *   d in {64, 128}; Hq % Hkv == 0; N >= 0; causal 0 or 1; any finite scale.
+ * Returns FA_OK or a status code above (FA_ERR_WORKSPACE for a missing or short
+ * workspace).
+ */
+int fa_bwd(const void* q, const void* k, const void* v, const void* o,
+           const float* lse, const void* dout, void* dq, void* dk, void* dv,
+           int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+           void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * fa_decode_paged_workspace_size -- bytes of device workspace fa_decode_paged
  * needs for these sizes (fp32 split partials and their logsumexps).  Returns 0
  * when an argument is out of range (negative size, unsupported d / page_size).

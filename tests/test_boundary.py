@@ -32,8 +32,8 @@ def L():
 
 def test_every_declared_symbol_is_exported(L):
     names = declared_functions()
-    assert set(names) >= {"fa_fwd", "fa_fwd_f32", "fa_decode_paged", "fa_decode_paged_workspace_size",
-                          "fa_status_string"}
+    assert set(names) >= {"fa_fwd", "fa_fwd_f32", "fa_bwd", "fa_bwd_workspace_size", "fa_decode_paged",
+                          "fa_decode_paged_workspace_size", "fa_status_string"}
     for n in names:
         assert hasattr(L, n), n
 
@@ -105,3 +105,37 @@ def test_workspace_size(L):
     assert fa.fa_decode_paged_workspace_size(1, 1, 96, 1, 16) == 0
     assert fa.fa_decode_paged_workspace_size(1, 1, 64, 1, 8) == 0
     assert fa.fa_decode_paged_workspace_size(-1, 1, 64, 1, 16) == 0
+
+
+def bwd(L, q=P, k=P, v=P, o=P, lse=P, do=P, dq=P, dk=P, dv=P, B=1, Hq=2, Hkv=1, N=16, d=64, causal=0, scale=0.125,
+        ws=P, wsb=1 << 30):
+    return L.fa_bwd(q, k, v, o, lse, do, dq, dk, dv, B, Hq, Hkv, N, d, causal, scale, ws, wsb, Z)
+
+
+def test_bwd_validation(L):
+    assert bwd(L, q=Z) == NULL
+    assert bwd(L, do=Z) == NULL
+    assert bwd(L, dk=Z) == NULL
+    assert bwd(L, d=96) == UNSUP
+    assert bwd(L, Hq=3, Hkv=2) == SHAPE
+    assert bwd(L, causal=5) == SHAPE
+    assert bwd(L, scale=float("nan")) == SCALE
+    assert bwd(L, dv=MIS) == ALIGN
+    assert bwd(L, ws=Z) == WORKSPACE
+    need = fa.fa_bwd_workspace_size(1, 2, 1, 16, 64)
+    assert bwd(L, wsb=need - 1) == WORKSPACE
+    assert bwd(L, ws=MIS, wsb=need) == ALIGN
+    assert bwd(L, q=Z, k=Z, v=Z, o=Z, lse=Z, do=Z, dq=Z, dk=Z, dv=Z, ws=Z, B=0) == OK
+
+
+def test_bwd_workspace_size(L):
+    # D per row (fp32, padded to 256 B); head-chunk partials of dK and dV only when
+    # fewer than 512 (128-key block, K/V head) pairs exist
+    def dbytes(B, Hq, N):
+        return -(-B * Hq * N * 4 // 256) * 256
+    assert fa.fa_bwd_workspace_size(1, 32, 32, 8192, 128) == dbytes(1, 32, 8192)      # 2048 pairs
+    assert fa.fa_bwd_workspace_size(2, 32, 8, 4096, 128) == dbytes(2, 32, 4096)       # 512 pairs
+    # multi-query: 64 pairs -> 8 chunks of 4 heads
+    assert fa.fa_bwd_workspace_size(2, 32, 1, 4096, 128) == dbytes(2, 32, 4096) + 2 * 8 * 2 * 1 * 4096 * 128 * 4
+    assert fa.fa_bwd_workspace_size(1, 2, 1, 16, 96) == 0
+    assert fa.fa_bwd_workspace_size(1, 3, 2, 16, 64) == 0
