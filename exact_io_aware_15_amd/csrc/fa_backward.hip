@@ -32,34 +32,40 @@
 namespace fa {
 namespace {
 
-constexpr int kBwdWaves = 4;                 // one wave per SIMD
+constexpr int kBwdWaves = 4;                 // dK/dV: one wave per SIMD
 constexpr int kBwdThreads = kBwdWaves * 64;
+#ifndef FA_BWD_DQ_WAVES
+#define FA_BWD_DQ_WAVES 8
+#endif
+constexpr int kDqWaves = FA_BWD_DQ_WAVES;    // dQ: two waves per SIMD
 constexpr int kWaveRows = 32;                // query rows (dQ) or keys (dK/dV) per wave
-constexpr int kBlockRows = kBwdWaves * kWaveRows;  // 128 per workgroup
+constexpr int kBlockRows = kBwdWaves * kWaveRows;  // 128 keys per dK/dV workgroup
+constexpr int kDqRows = kDqWaves * kWaveRows;      // 256 query rows per dQ workgroup
 constexpr int kTile = 64;                    // rows of the streamed operand per tile
 
-template <int D>
+template <int D, int W = kBwdWaves>
 struct BLay {
   static constexpr int ROWB = D * 2;              // bytes per row
   static constexpr int CPR = ROWB / 16;           // 16-byte chunks per row
   static constexpr int RPB = 1024 / ROWB;         // rows per 1 KB block
   static constexpr int TBYTES = kTile * ROWB;     // one tile
-  static constexpr int BPW = TBYTES / 1024 / kBwdWaves;  // 1 KB blocks copied per wave
-  static_assert(BPW * kBwdWaves * 1024 == TBYTES, "tile copy must split evenly over the waves");
+  static constexpr int BPW = TBYTES / 1024 / W;  // 1 KB blocks copied per wave (W waves)
+  static_assert(BPW * W * 1024 == TBYTES, "tile copy must split evenly over the waves");
   // physical chunk = logical chunk ^ swz(row); depends on row & 15 only
   __host__ __device__ static constexpr int swz(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
 };
 
 typedef short s16x8 __attribute__((ext_vector_type(8)));
 
-// HBM -> LDS copy of tile rows r0 .. r0+63 of one (batch, head) slice: this wave's
-// 1 KB blocks w, w + 4, ...  Block w + 4i lies 4 KB after block w in both HBM and
-// LDS and the swizzle repeats with that period, so one per-lane offset cp serves all.
-template <int D>
+// HBM -> LDS copy of tile rows r0 .. r0+63 of one (batch, head) slice by W waves:
+// this wave's 1 KB blocks w, w + W, ...  Block w + Wi lies W KB after block w in
+// both HBM and LDS and the swizzle repeats with that period, so one per-lane
+// offset cp serves all.
+template <int D, int W = kBwdWaves>
 __device__ __forceinline__ void copy_tile(uint8_t* dst, const void* base, uint32_t bytes, uint32_t cp, int r0, int w) {
-  using L = BLay<D>;
-  constexpr uint32_t kStride = kBwdWaves * 1024;
-  static_assert((kStride / L::ROWB) % 16 == 0, "swizzle must repeat every kBwdWaves blocks");
+  using L = BLay<D, W>;
+  constexpr uint32_t kStride = W * 1024;
+  static_assert((kStride / L::ROWB) % 16 == 0, "swizzle must repeat every W blocks");
   const auto rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
   const uint32_t off = (uint32_t)r0 * L::ROWB + cp;
 #pragma unroll
@@ -78,9 +84,9 @@ __device__ __forceinline__ void copy_rowvals(float* dst, const float* base, int 
 }
 
 // Lane's byte offset for copying block w of a tile (row w*RPB + lane/CPR, swizzled chunk).
-template <int D>
+template <int D, int W = kBwdWaves>
 __device__ __forceinline__ uint32_t copy_offset(int w, int lane) {
-  using L = BLay<D>;
+  using L = BLay<D, W>;
   const int r = w * L::RPB + lane / L::CPR;
   return r * L::ROWB + (((lane % L::CPR) ^ L::swz(r)) << 4);
 }
@@ -110,6 +116,20 @@ __device__ __forceinline__ bf16x8 tr_frag(const uint8_t* base, int lo, int up) {
 
 __device__ __forceinline__ u32x4 ld16(const uint16_t* p) { return *reinterpret_cast<const u32x4*>(p); }
 
+// Scheduling pattern for a run of `mfmas` MFMAs that each consume `reads` LDS
+// reads: keep the reads of `ahead` MFMAs in flight ahead of their use.
+template <int mfmas, int reads, int id, int ahead>
+__device__ __forceinline__ void sched_reads_ahead() {
+  constexpr int pre = ahead < mfmas ? ahead : mfmas;
+  __builtin_amdgcn_sched_group_barrier(0x100, pre * reads, id);
+#pragma unroll
+  for (int i = 0; i < mfmas - pre; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, id);
+    __builtin_amdgcn_sched_group_barrier(0x100, reads, id);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, pre, id);
+}
+
 // ---------------------------------------------------------------------------
 // D = rowsum(dO * O): D/8 lanes per row, 16-byte loads, DPP reduction.
 template <int D>
@@ -137,16 +157,21 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(const uint16_t* __restri
 // ---------------------------------------------------------------------------
 // dQ: one workgroup per (128-row query block, query head, batch), four waves of 32
 // rows.  K and V tiles of 64 keys stream through LDS (two buffers each).
+// LDS reads kept ahead of the MFMAs (measured: deeper pays off at d = 64)
+template <int D>
+constexpr int ahead_for() { return D == 64 ? 6 : 2; }
+
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(
+__global__ __launch_bounds__(kDqWaves * 64, 1) void bwd_dq_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ Lse, const float* __restrict__ Dlt,
     uint16_t* __restrict__ dQ, int B, int Hq, int Hkv, int N, float cs /* scale * log2 e */, float scale) {
-  using L = BLay<D>;
+  using L = BLay<D, kDqWaves>;
   constexpr int KK = D / 16, DB = D / 32;
+  constexpr int kAhead = ahead_for<D>();
   __shared__ __attribute__((aligned(16))) uint8_t smem[4 * L::TBYTES];  // K[2], V[2]
 
-  const int nqb = (N + kBlockRows - 1) / kBlockRows;
+  const int nqb = (N + kDqRows - 1) / kDqRows;
   const int BH = B * Hq;
   const int qb = CAUSAL ? (nqb - 1 - (int)(blockIdx.x / BH)) : (int)(blockIdx.x / BH);  // heaviest first
   const int bh = blockIdx.x % BH;
@@ -156,7 +181,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
-  const int rw0 = qb * kBlockRows + w * kWaveRows;
+  const int rw0 = qb * kDqRows + w * kWaveRows;
   const int qrow = rw0 + l32;
   const bool row_ok = qrow < N;
 
@@ -192,14 +217,14 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(
   for (int kk = 0; kk < KK; ++kk) roff[kk] = l32 * L::ROWB + (((2 * kk + hi) ^ L::swz(l32)) << 4);
   int tlo[DB], thi[DB];
   tr_offsets<D>(lane, tlo, thi);
-  const uint32_t cp = copy_offset<D>(w, lane);
+  const uint32_t cp = copy_offset<D, kDqWaves>(w, lane);
 
-  const int kend = CAUSAL ? min(N, (qb + 1) * kBlockRows) : N;
+  const int kend = CAUSAL ? min(N, (qb + 1) * kDqRows) : N;
   const int ntiles = (kend + kTile - 1) / kTile;
 
   if (ntiles > 0) {
-    copy_tile<D>(smem, kbase, head_bytes, cp, 0, w);
-    copy_tile<D>(smem + 2 * L::TBYTES, vbase, head_bytes, cp, 0, w);
+    copy_tile<D, kDqWaves>(smem, kbase, head_bytes, cp, 0, w);
+    copy_tile<D, kDqWaves>(smem + 2 * L::TBYTES, vbase, head_bytes, cp, 0, w);
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   __syncthreads();
@@ -211,8 +236,8 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(
       if (t >= ntiles) break;
       const int j0 = t * kTile;
       if (t + 1 < ntiles) {
-        copy_tile<D>(smem + (1 - u) * L::TBYTES, kbase, head_bytes, cp, j0 + kTile, w);
-        copy_tile<D>(smem + (3 - u) * L::TBYTES, vbase, head_bytes, cp, j0 + kTile, w);
+        copy_tile<D, kDqWaves>(smem + (1 - u) * L::TBYTES, kbase, head_bytes, cp, j0 + kTile, w);
+        copy_tile<D, kDqWaves>(smem + (3 - u) * L::TBYTES, vbase, head_bytes, cp, j0 + kTile, w);
       }
       const bool skip = CAUSAL && (j0 > rw0 + kWaveRows - 1);
       if (!skip) {
@@ -241,6 +266,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(
             const bf16x8 vf = *reinterpret_cast<const bf16x8*>(vb + a * 32 * L::ROWB + roff[kk]);
             dp[a] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, gf[kk], dp[a], 0, 0, 0);
           }
+        sched_reads_ahead<4 * KK, 1, 0, kAhead>();
         // dS^T = P^T * (dP^T - D), masked keys (after the row, or past N) give 0
         const bool need_mask = CAUSAL ? (j0 + kTile - 1 > rw0) : (j0 + kTile > N);
         const int lim = (CAUSAL ? qrow - j0 : N - 1 - j0) - 4 * hi;
@@ -276,6 +302,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(
               acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag(grp0, tlo[db], thi[db]), dsb[a][h2], acc[db],
                                                                 0, 0, 0);
             }
+        sched_reads_ahead<4 * DB, 2, 1, kAhead>();
       }
       __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): tile t+1 has landed
       __syncthreads();
@@ -336,6 +363,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(
     int B, int Hq, int Hkv, int N, int heads_per_chunk, int nchunks, float cs, float scale) {
   using L = BLay<D>;
   constexpr int KK = D / 16, DB = D / 32;
+  constexpr int kAhead = ahead_for<D>();
   __shared__ __attribute__((aligned(16))) uint8_t smem[4 * L::TBYTES];  // Q[2], dO[2]
   __shared__ __attribute__((aligned(16))) float rowv[2][2][kTile];      // [buffer][L, D][row]
 
@@ -428,6 +456,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(
             const bf16x8 ga = *reinterpret_cast<const bf16x8*>(gb_ + rb * 32 * L::ROWB + roff[kk]);
             dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga, vf[kk], dp, 0, 0, 0);
           }
+          sched_reads_ahead<2 * KK, 1, 2, kAhead>();
           // P and dS for the lane's key and 16 rows; row values from LDS, 4 rows per read
           bf16x8 pb[2], dsb[2];
 #pragma unroll
@@ -468,6 +497,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(
               dka[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dsb[s2], tr_frag(qb_ + r0g, tlo[db], thi[db]), dka[db],
                                                                 0, 0, 0);
             }
+          sched_reads_ahead<4 * DB, 2, 3, kAhead>();
         }
       }
       __builtin_amdgcn_s_waitcnt(0x0F70);
@@ -524,13 +554,14 @@ hipError_t launch_bwd_t(const BwdArgs& a) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const float cs = a.scale * kLog2e;
-  const int nqb = (a.N + kBlockRows - 1) / kBlockRows;
-  hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)(nqb * a.B * a.Hq)), dim3(kBwdThreads), 0, st,
+  const int nqb_dq = (a.N + kDqRows - 1) / kDqRows;
+  hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)(nqb_dq * a.B * a.Hq)), dim3(kDqWaves * 64), 0, st,
                      (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (const uint16_t*)a.dout, a.lse,
                      dlt, (uint16_t*)a.dq, a.B, a.Hq, a.Hkv, a.N, cs, a.scale);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)(nqb * a.B * a.Hkv * pl.nchunks)),
+  const int nkb = (a.N + kBlockRows - 1) / kBlockRows;
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)(nkb * a.B * a.Hkv * pl.nchunks)),
                      dim3(kBwdThreads), 0, st, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                      (const uint16_t*)a.dout, a.lse, dlt, (uint16_t*)a.dk, (uint16_t*)a.dv, partK, partV, a.B, a.Hq,
                      a.Hkv, a.N, pl.heads_per_chunk, pl.nchunks, cs, a.scale);
