@@ -49,6 +49,7 @@ def source_digest(files):
 KERNEL_SOURCES = {
     "prefill": ["fa_device.h", "fa_launch.h", "fa_prefill_bf16.hip"],
     "decode": ["fa_device.h", "fa_launch.h", "fa_decode.hip"],
+    "backward": ["fa_device.h", "fa_launch.h", "fa_backward.hip"],
 }
 
 
@@ -101,6 +102,30 @@ def cpu_baseline_prefill(x, cfg, stride):
             "seconds": round(dt, 2)}
 
 
+def cpu_baseline_backward(x, do, cfg, heads):
+    """fp64 oracle gradients for the first `heads` query heads (and their K/V heads) of batch 0."""
+    import numpy as np
+    import threadpoolctl
+
+    from oracle import attention_bwd_ref
+
+    G = cfg.Hq // cfg.Hkv
+    nkv = -(-heads // G)
+    q = x["q"][:1, :heads].float().numpy()
+    k = x["k"][:1, :nkv].float().numpy()
+    v = x["v"][:1, :nkv].float().numpy()
+    g = do[:1, :heads].float().numpy()
+    t0 = time.perf_counter()
+    attention_bwd_ref(q, k, v, g, cfg.causal, cfg.scale)
+    dt = time.perf_counter() - t0
+    flops = 2.5 * 4.0 * heads * cfg.N * cfg.N * cfg.d / (2 if cfg.causal else 1)
+    threads = max(i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()) or 1
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{heads} of {cfg.B * cfg.Hq} query heads of {cfg.name} (every row and key); "
+                      f"{dt:.1f} s of fp64 numpy",
+            "seconds": round(dt, 2)}
+
+
 def cpu_baseline_decode(x, cfg, nseq):
     import numpy as np
     import threadpoolctl
@@ -132,10 +157,14 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-row-stride", type=int, default=1,
                     help="oracle baseline on every n-th query row of the prefill (1 = the whole workload)")
+    ap.add_argument("--cpu-bwd-heads", type=int, default=1,
+                    help="oracle backward baseline on the first n query heads of batch 0")
     ap.add_argument("--cpu-decode-seqs", type=int, default=64,
                     help="oracle baseline on the first n sequences of the decode (64 = the whole workload)")
-    ap.add_argument("--only", choices=["prefill", "decode"], default=None,
-                    help="time one half of the step only (for profiling runs)")
+    ap.add_argument("--only", choices=["prefill", "decode", "backward"], default=None,
+                    help="time one part only (for profiling runs)")
+    ap.add_argument("--no-bwd", action="store_true",
+                    help="skip the backward measurement (reported beside the step, not part of it)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB 5 times (calibrates the "
                          "FETCH_SIZE / WRITE_SIZE counters against a known byte count) and exit")
@@ -167,6 +196,7 @@ def main():
     pcfg, dcfg = CONFIGS[PREFILL], CONFIGS[DECODE]
     run_p = args.only in (None, "prefill")
     run_d = args.only in (None, "decode")
+    run_b = args.only == "backward" or (args.only is None and not args.no_bwd)
 
     log("generating inputs")
     px = make_inputs(pcfg) if run_p else None
@@ -218,6 +248,45 @@ def main():
     step_ms = ev[0][0].elapsed_time(ev[-1][2]) / K
     log(f"prefill {p_ms:.4f} ms, decode {d_ms:.4f} ms, step {step_ms:.4f} ms (wall {wall * 1e3 / K:.4f} ms)")
 
+    bwd = None
+    if run_b:
+        # the backward (not part of the step): gradients of the same causal prefill for a
+        # seeded upstream gradient, with O and L from the forward computed beforehand
+        from exact_io_aware_15_amd.workloads import make_grad_output
+        bx = px if px is not None else make_inputs(pcfg)
+        bq, bk, bv = (bx[n].to(dev) for n in "qkv")
+        bdo_cpu = make_grad_output(pcfg.B, pcfg.Hq, pcfg.N, pcfg.d, seed=pcfg.seed)
+        bdo = bdo_cpu.to(dev)
+        bo, bl = fa.fa_fwd(bq, bk, bv, causal=pcfg.causal, scale=pcfg.scale)
+        bws = torch.empty(max(16, fa.fa_bwd_workspace_size(pcfg.B, pcfg.Hq, pcfg.Hkv, pcfg.N, pcfg.d)),
+                          dtype=torch.uint8, device=dev)
+        bdq, bdk, bdv = torch.empty_like(bq), torch.empty_like(bk), torch.empty_like(bv)
+
+        def backward():
+            fa.fa_bwd(bq, bk, bv, bo, bl, bdo, causal=pcfg.causal, scale=pcfg.scale, dq=bdq, dk=bdk, dv=bdv,
+                      workspace=bws)
+
+        for _ in range(max(1, args.warmup // 3)):
+            backward()
+        torch.cuda.synchronize()
+        bev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
+        for i in range(K):
+            bev[i][0].record()
+            backward()
+            bev[i][1].record()
+        torch.cuda.synchronize()
+        b_ms = sum(e[0].elapsed_time(e[1]) for e in bev) / K
+        bfl = 2.5 * prefill_flops(pcfg)
+        btf = bfl / (b_ms * 1e-3) / 1e12
+        log(f"backward {b_ms:.4f} ms ({btf:.1f} TFLOP/s)")
+        bwd = {"value": round(btf, 2), "unit": "TFLOP/s", "ms": round(b_ms, 5),
+               "roofline": {"bound": "mfma", "achieved": round(btf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                            "frac": round(btf / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic("backward"),
+                            "kernel": "bwd_delta + bwd_dq + bwd_dkdv <128, causal>",
+                            "algorithmic_flops_per_launch": bfl},
+               "workload": "gradients of the causal bf16 prefill B1 Hq32 N8192 d128 (dO ~ N(0,1)); FLOPs 2.5x the "
+                           "forward's (five N x N x d products), causal half"}
+
     res = {"metric": METRIC, "n_gpus": 1, "steps": K, "warmup": args.warmup, "ms_per_step": round(step_ms, 5),
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
            "data": "synthetic (seeded N(0,1) inputs; random page permutation)"}
@@ -248,6 +317,10 @@ def main():
                               "seed": dcfg.seed}
         if not run_p:
             res.update({"value": dec["value"], "unit": "GB/s", "roofline": dec["roofline"]})
+    if bwd is not None:
+        res["backward"] = bwd
+        if not run_p and not run_d:
+            res.update({"value": bwd["value"], "unit": "TFLOP/s", "roofline": bwd["roofline"]})
     res["config"] = cfg_desc
     if not args.no_cpu_baseline:
         log("timing the fp64 CPU oracle on a bounded sample")
@@ -259,6 +332,12 @@ def main():
                 res["decode"]["cpu_baseline"] = cb
             else:
                 res["cpu_baseline"] = cb
+        if bwd is not None:
+            bcb = cpu_baseline_backward(bx, bdo_cpu, pcfg, args.cpu_bwd_heads)
+            if "cpu_baseline" in res:
+                res["backward"]["cpu_baseline"] = bcb
+            else:
+                res["cpu_baseline"] = bcb
     print(json.dumps(res), flush=True)
 
 
