@@ -19,6 +19,7 @@ differences, identities).  Nothing here is "parity unpinned".
 
 from .attention import (  # noqa: F401
     attention_ref,
+    alibi_slopes_ref,
     decode_ref,
     online_ref,
     lse_merge_ref,

@@ -26,6 +26,7 @@ import numpy as np
 
 __all__ = [
     "attention_ref",
+    "alibi_slopes_ref",
     "decode_ref",
     "online_ref",
     "lse_merge_ref",
@@ -63,7 +64,8 @@ def _softmax_rows(s: np.ndarray, v: np.ndarray):
     return o, lse
 
 
-def attention_ref(q, k, v, causal: bool, scale: float, rows=None, chunk: int = 1024):
+def attention_ref(q, k, v, causal: bool, scale: float, rows=None, chunk: int = 1024, window: int = 0,
+                  alibi_slopes=None):
     """Standard (materialising) attention: S = scale * Q K^T, mask, softmax, P V.
 
     "Phase 08", Lab 01 step 1 (standard attention as the reference) and the
@@ -74,6 +76,13 @@ def attention_ref(q, k, v, causal: bool, scale: float, rows=None, chunk: int = 1
     rows: optional 1-D array of query-row indices to evaluate (all rows if None).
     Each evaluated row's full score vector over all N keys is formed; rows are
     taken `chunk` at a time only to bound memory.
+
+    Extensions named in the "Phase 08" Lab 01 extensions row (sliding-window
+    attention as in Mistral, ALiBi bias):
+      window: W >= 1 keeps, for query i, only keys j >= i - W + 1 (the last W
+        positions up to and including i); causal only; 0 = no window.
+      alibi_slopes: per query head slope m_h (sequence of Hq floats); the score of
+        (i, j) gains -m_h * |i - j| (= m_h * (j - i) under the causal mask).
     """
     q = _f64(q)
     k = _f64(k)
@@ -82,7 +91,10 @@ def attention_ref(q, k, v, causal: bool, scale: float, rows=None, chunk: int = 1
     Bk, Hkv, Nk, dk = k.shape
     if (Bk, Nk, dk) != (B, N, d) or v.shape != k.shape:
         raise ValueError("q/k/v shapes disagree")
+    if window and not causal:
+        raise ValueError("a sliding window is defined for causal attention only")
     G = _group_size(Hq, Hkv)
+    slopes = None if alibi_slopes is None else _f64(alibi_slopes)
     row_idx = np.arange(N) if rows is None else np.asarray(rows, dtype=np.int64)
     R = row_idx.shape[0]
     O = np.zeros((B, Hq, R, d), dtype=np.float64)
@@ -96,12 +108,22 @@ def attention_ref(q, k, v, causal: bool, scale: float, rows=None, chunk: int = 1
             for c0 in range(0, R, chunk):
                 ri = row_idx[c0:c0 + chunk]
                 s = scale * (q[b, h, ri] @ kh.T)  # [r, N], every key of every row
+                if slopes is not None:
+                    s = s - slopes[h] * np.abs(ri[:, None] - key_idx[None, :])
                 if causal:
                     s = np.where(key_idx[None, :] <= ri[:, None], s, -np.inf)
+                if window:
+                    s = np.where(key_idx[None, :] >= ri[:, None] - window + 1, s, -np.inf)
                 o, lse = _softmax_rows(s, vh)
                 O[b, h, c0:c0 + chunk] = o
                 L[b, h, c0:c0 + chunk] = lse
     return O, L
+
+
+def alibi_slopes_ref(n_heads: int):
+    """The geometric ALiBi slopes 2^(-8 (h + 1) / n) for heads h = 0 .. n-1 (n a power of
+    two), the usual choice with the bias of the Lab 01 extensions row."""
+    return np.array([2.0 ** (-8.0 * (h + 1) / n_heads) for h in range(n_heads)])
 
 
 def gather_pages_ref(pages, page_table_row, ctx_len: int, kv_head: int) -> np.ndarray:

@@ -9,8 +9,9 @@ list and Lab 01 step 1 (standard attention), screna.ai FlashAttention block
 import math
 
 
-def brute_attention(q, k, v, causal, scale):
-    """q: nested lists [B][Hq][N][d]; k, v: [B][Hkv][N][d]. Returns (O, L) nested lists."""
+def brute_attention(q, k, v, causal, scale, window=0, slopes=None):
+    """q: nested lists [B][Hq][N][d]; k, v: [B][Hkv][N][d]. Returns (O, L) nested lists.
+    window W: only keys j >= i - W + 1 (0 = none); slopes: ALiBi bias -slope[h] * |i - j|."""
     B = len(q)
     Hq = len(q[0])
     Hkv = len(k[0])
@@ -23,8 +24,10 @@ def brute_attention(q, k, v, causal, scale):
             vh = v[b][h // G]
             Oh, Lh = [], []
             for i, qi in enumerate(q[b][h]):
-                visible = [j for j in range(len(kh)) if (not causal) or j <= i]
-                scores = [scale * math.fsum(qi[t] * kh[j][t] for t in range(len(qi))) for j in visible]
+                visible = [j for j in range(len(kh)) if ((not causal) or j <= i) and (not window or j >= i - window + 1)]
+                bias = [0.0 if slopes is None else -slopes[h] * abs(i - j) for j in visible]
+                scores = [scale * math.fsum(qi[t] * kh[j][t] for t in range(len(qi))) + bias[n]
+                          for n, j in enumerate(visible)]
                 top = max(scores)
                 w = [math.exp(s - top) for s in scores]
                 tot = math.fsum(w)

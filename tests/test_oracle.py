@@ -360,3 +360,79 @@ def test_decode_empty_context():
     kp = np.full((2, 1, 16, 4), np.nan)
     O, L = decode_ref(np.ones((1, 2, 4)), kp, kp, np.array([[1]]), np.array([0]), 1.0)
     assert np.all(O == 0) and np.all(np.isneginf(L))
+
+
+# ------------------------------------------------- sliding window and ALiBi (Lab 01 extensions)
+
+from oracle import alibi_slopes_ref  # noqa: E402
+
+
+@pytest.mark.parametrize("window", [1, 2, 3, 5, 100])
+@pytest.mark.parametrize("alibi", [False, True])
+def test_window_alibi_matches_brute_force(window, alibi):
+    B, Hq, Hkv, N, d = 1, 2, 1, 6, 3
+    q, k, v = _rand((B, Hq, N, d), 60), _rand((B, Hkv, N, d), 61), _rand((B, Hkv, N, d), 62)
+    slopes = [0.5, 0.125] if alibi else None
+    O, L = attention_ref(q, k, v, True, 0.8, window=window, alibi_slopes=slopes)
+    Ob, Lb = brute_attention(q.tolist(), k.tolist(), v.tolist(), True, 0.8, window=window, slopes=slopes)
+    np.testing.assert_allclose(O, np.array(Ob), rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(L, np.array(Lb), rtol=1e-13, atol=1e-13)
+
+
+def test_alibi_noncausal_matches_brute_force():
+    q, k, v = _rand((1, 2, 5, 3), 63), _rand((1, 2, 5, 3), 64), _rand((1, 2, 5, 3), 65)
+    O, L = attention_ref(q, k, v, False, 0.6, alibi_slopes=[0.3, 2.0])
+    Ob, Lb = brute_attention(q.tolist(), k.tolist(), v.tolist(), False, 0.6, slopes=[0.3, 2.0])
+    np.testing.assert_allclose(O, np.array(Ob), rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(L, np.array(Lb), rtol=1e-13, atol=1e-13)
+
+
+def test_window_one_selects_the_diagonal():
+    # W = 1: each row sees only its own key, so O_i = V_i and L_i = scale q_i . k_i
+    q, k, v = _rand((2, 3, 9, 4), 66), _rand((2, 3, 9, 4), 67), _rand((2, 3, 9, 4), 68)
+    O, L = attention_ref(q, k, v, True, 0.7, window=1)
+    np.testing.assert_allclose(O, v, rtol=0, atol=1e-15)
+    np.testing.assert_allclose(L, 0.7 * np.sum(q * k, axis=-1), rtol=1e-14, atol=1e-14)
+
+
+def test_window_at_least_n_is_plain_causal():
+    q, k, v = _rand((1, 2, 11, 4), 69), _rand((1, 2, 11, 4), 70), _rand((1, 2, 11, 4), 71)
+    a = attention_ref(q, k, v, True, 0.5, window=11)
+    b = attention_ref(q, k, v, True, 0.5)
+    np.testing.assert_array_equal(a[0], b[0])
+    np.testing.assert_array_equal(a[1], b[1])
+
+
+def test_alibi_zero_slope_is_plain_and_steep_slope_picks_diagonal():
+    q, k, v = _rand((1, 2, 8, 4), 72), _rand((1, 2, 8, 4), 73), _rand((1, 2, 8, 4), 74)
+    a = attention_ref(q, k, v, True, 0.5, alibi_slopes=[0.0, 0.0])
+    b = attention_ref(q, k, v, True, 0.5)
+    np.testing.assert_array_equal(a[0], b[0])
+    # a slope of 1e4 per position drives every other key's weight below exp(-1e4) = 0
+    O, _ = attention_ref(q, k, v, True, 0.5, alibi_slopes=[1e4, 1e4])
+    np.testing.assert_allclose(O, v, rtol=0, atol=1e-15)
+
+
+def test_alibi_shift_form_under_causal_mask():
+    # with j <= i, -m |i - j| = m j - m i; the -m i part is constant along row i, so
+    # the probabilities are those of the scores plus m j, and L is their logsumexp
+    # minus m i
+    N, d, m = 7, 3, 0.37
+    q, k, v = _rand((1, 1, N, d), 75), _rand((1, 1, N, d), 76), _rand((1, 1, N, d), 77)
+    O, L = attention_ref(q, k, v, True, 0.9, alibi_slopes=[m])
+    s = 0.9 * q[0, 0] @ k[0, 0].T + m * np.arange(N)[None, :]
+    s = np.where(np.tril(np.ones((N, N), bool)), s, -np.inf)
+    p = np.exp(s - s.max(axis=1, keepdims=True))
+    np.testing.assert_allclose(O[0, 0], (p @ v[0, 0]) / p.sum(axis=1, keepdims=True), rtol=1e-13, atol=1e-13)
+    lse = s.max(axis=1) + np.log(p.sum(axis=1)) - m * np.arange(N)
+    np.testing.assert_allclose(L[0, 0], lse, rtol=1e-13, atol=1e-13)
+
+
+def test_alibi_slopes_are_the_geometric_sequence():
+    s = alibi_slopes_ref(8)
+    np.testing.assert_allclose(s, [0.5 ** (h + 1) for h in range(8)], rtol=0, atol=0)
+
+
+def test_window_requires_causal():
+    with pytest.raises(ValueError):
+        attention_ref(np.zeros((1, 1, 2, 2)), np.zeros((1, 1, 2, 2)), np.zeros((1, 1, 2, 2)), False, 1.0, window=1)
