@@ -163,6 +163,8 @@ def main():
                     help="oracle baseline on the first n sequences of the decode (64 = the whole workload)")
     ap.add_argument("--only", choices=["prefill", "decode", "backward"], default=None,
                     help="time one part only (for profiling runs)")
+    ap.add_argument("--no-window", action="store_true",
+                    help="skip the sliding-window + ALiBi measurement (reported beside the step)")
     ap.add_argument("--no-bwd", action="store_true",
                     help="skip the backward measurement (reported beside the step, not part of it)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -287,6 +289,41 @@ def main():
                "workload": "gradients of the causal bf16 prefill B1 Hq32 N8192 d128 (dO ~ N(0,1)); FLOPs 2.5x the "
                            "forward's (five N x N x d products), causal half"}
 
+    wa = None
+    if run_b and not args.no_window:
+        # sliding window (W = 4096) + ALiBi on the same causal prefill (not part of the step);
+        # FLOPs count only the visible (query, key) pairs: sum_i min(i + 1, W)
+        from exact_io_aware_15_amd.workloads import make_alibi_slopes
+        W = 4096
+        slopes = make_alibi_slopes(pcfg.Hq).to(dev)
+        wo, wl = torch.empty_like(bq), torch.empty((pcfg.B, pcfg.Hq, pcfg.N), dtype=torch.float32, device=dev)
+
+        def windowed():
+            fa.fa_fwd_ex(bq, bk, bv, causal=True, scale=pcfg.scale, window=W, alibi_slopes=slopes, out=wo, lse=wl)
+
+        for _ in range(max(1, args.warmup // 3)):
+            windowed()
+        torch.cuda.synchronize()
+        wev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
+        for i in range(K):
+            wev[i][0].record()
+            windowed()
+            wev[i][1].record()
+        torch.cuda.synchronize()
+        w_ms = sum(e[0].elapsed_time(e[1]) for e in wev) / K
+        n = pcfg.N
+        pairs = W * (W + 1) // 2 + (n - W) * W
+        wfl = 4.0 * pcfg.B * pcfg.Hq * pcfg.d * pairs
+        wtf = wfl / (w_ms * 1e-3) / 1e12
+        log(f"window+alibi {w_ms:.4f} ms ({wtf:.1f} TFLOP/s)")
+        wa = {"value": round(wtf, 2), "unit": "TFLOP/s", "ms": round(w_ms, 5),
+              "roofline": {"bound": "mfma", "achieved": round(wtf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                           "frac": round(wtf / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                           "kernel": "fwd_bf16_kernel<128, causal, window/ALiBi>",
+                           "algorithmic_flops_per_launch": wfl},
+              "workload": f"causal bf16 prefill B1 Hq32 N8192 d128 with a {W}-key sliding window and ALiBi "
+                          "slopes 2^(-8(h+1)/32); FLOPs over visible pairs only"}
+
     res = {"metric": METRIC, "n_gpus": 1, "steps": K, "warmup": args.warmup, "ms_per_step": round(step_ms, 5),
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
            "data": "synthetic (seeded N(0,1) inputs; random page permutation)"}
@@ -317,6 +354,8 @@ def main():
                               "seed": dcfg.seed}
         if not run_p:
             res.update({"value": dec["value"], "unit": "GB/s", "roofline": dec["roofline"]})
+    if wa is not None:
+        res["window_alibi"] = wa
     if bwd is not None:
         res["backward"] = bwd
         if not run_p and not run_d:

@@ -21,6 +21,7 @@ __all__ = [
     "lib",
     "fa_fwd",
     "fa_fwd_f32",
+    "fa_fwd_ex",
     "fa_bwd",
     "fa_bwd_workspace_size",
     "fa_decode_paged",
@@ -54,6 +55,8 @@ def lib() -> ctypes.CDLL:
     L.fa_fwd.restype = i
     L.fa_fwd_f32.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp]
     L.fa_fwd_f32.restype = i
+    L.fa_fwd_ex.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp, vp]
+    L.fa_fwd_ex.restype = i
     L.fa_bwd_workspace_size.argtypes = [i, i, i, i, i]
     L.fa_bwd_workspace_size.restype = sz
     L.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp, sz, vp]
@@ -125,6 +128,32 @@ def fa_fwd(q, k, v, causal=False, scale=None, out=None, lse=None):
 def fa_fwd_f32(q, k, v, causal=False, scale=None, out=None, lse=None):
     """fp32 forward, same layouts as fa_fwd."""
     return _fwd("fa_fwd_f32", torch.float32, q, k, v, causal, scale, out, lse)
+
+
+def fa_fwd_ex(q, k, v, causal=True, scale=None, window=0, alibi_slopes=None, out=None, lse=None):
+    """bf16 forward with a sliding window (causal, last `window` keys; 0 = none) and/or
+    ALiBi slopes (fp32 [Hq] on the device, bias -m_h |i - j|; None = no bias)."""
+    B, Hq, N, d = q.shape
+    Hkv = k.shape[1]
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on a GPU")
+    _need(q, "q", torch.bfloat16, (B, Hq, N, d), dev)
+    _need(k, "k", torch.bfloat16, (B, Hkv, N, d), dev)
+    _need(v, "v", torch.bfloat16, (B, Hkv, N, d), dev)
+    if alibi_slopes is not None:
+        _need(alibi_slopes, "alibi_slopes", torch.float32, (Hq,), dev)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    out = torch.empty((B, Hq, N, d), dtype=torch.bfloat16, device=dev) if out is None else out
+    lse = torch.empty((B, Hq, N), dtype=torch.float32, device=dev) if lse is None else lse
+    _need(out, "out", torch.bfloat16, (B, Hq, N, d), dev)
+    _need(lse, "lse", torch.float32, (B, Hq, N), dev)
+    st = lib().fa_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv, N, d, int(bool(causal)),
+                         float(scale), int(window), _ptr(alibi_slopes), _stream(q))
+    if st != FA_OK:
+        raise FAError(st, "fa_fwd_ex")
+    return out, lse
 
 
 def fa_bwd_workspace_size(B, Hq, Hkv, N, d) -> int:

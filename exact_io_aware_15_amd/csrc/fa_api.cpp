@@ -69,6 +69,19 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
   return finish(fa::launch_fwd_bf16(a), stream);
 }
 
+int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv, int N,
+              int d, int causal, float scale, int window, const float* alibi_slopes, void* stream) {
+  bool empty = false;
+  const int st = check_fwd(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, scale, &empty);
+  if (st != FA_OK) return st;
+  if (window < 0) return FA_ERR_SHAPE;
+  if (window > 0 && !causal) return FA_ERR_UNSUPPORTED;
+  if (empty) return FA_OK;
+  if (alibi_slopes && ((uintptr_t)alibi_slopes & 3u) != 0) return FA_ERR_ALIGN;
+  fa::FwdArgs a{q, k, v, o, lse, B, Hq, Hkv, N, d, causal != 0, scale, stream, window, alibi_slopes};
+  return finish(fa::launch_fwd_bf16(a), stream);
+}
+
 size_t fa_bwd_workspace_size(int B, int Hq, int Hkv, int N, int d) {
   if (B < 0 || N < 0 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || (d != 64 && d != 128)) return 0;
   return fa::bwd_plan(B, Hq, Hkv, N, d).bytes;

@@ -18,6 +18,8 @@ struct FwdArgs {
   bool causal;
   float scale;
   void* stream;
+  int window = 0;                 // bf16 only: keys j >= i - window + 1 (0: none)
+  const float* slopes = nullptr;  // bf16 only: ALiBi slope per query head, or none
 };
 
 struct DecodeArgs {

@@ -133,12 +133,15 @@ __device__ __forceinline__ float tile_rowmax(f32x16 (&s)[2], int lim, float c) {
 
 // Raise the running max of rows whose tile max exceeds it by more than the
 // threshold, rescaling O and the sums.  Wave-uniform branch.
-template <int D>
+// SAFE: a row may still be at m_run = -inf when another row of the wave grows (only
+// with a sliding window); its factor is then 0 (its O and sums are still zero).
+template <int D, bool SAFE = false>
 __device__ __forceinline__ void maybe_rescale(WaveState<D>& st, float mt) {
   const bool grow = mt > st.m_run + kRescaleThreshold;
   if (__builtin_amdgcn_ballot_w64(grow) != 0) {
     const float mnew = fmaxf(st.m_run, mt);
-    const float alpha = exp2_fast(st.m_run - mnew);  // m_run = -inf -> 0
+    float alpha = exp2_fast(st.m_run - mnew);  // m_run = -inf, mnew finite -> 0
+    if (SAFE && st.m_run == -INFINITY) alpha = 0.f;
     st.l_exact *= alpha;
     st.l_round *= alpha;
 #pragma unroll
@@ -152,10 +155,12 @@ __device__ __forceinline__ void maybe_rescale(WaveState<D>& st, float mt) {
 // exp2 of the scores against the running max, packed to bf16 as the B operand of
 // the P V product; fp32 and bf16-rounded row sums.  Masked scores are -inf and
 // c > 0, so their probability is exactly 0.
-template <int D>
+// SAFE: the row may not have seen a visible key yet (m_run = -inf, possible only
+// with a sliding window); its masked scores then give exp2(-inf - 0) = 0.
+template <int D, bool SAFE = false>
 __device__ __forceinline__ void softmax_pack(const f32x16 (&s)[2], WaveState<D>& st, float c,
                                              bf16x8 (&pb)[2][2]) {
-  const float m = st.m_run;
+  const float m = (SAFE && st.m_run == -INFINITY) ? 0.f : st.m_run;
   const bf16x2 ones = as_bf16x2(0x3f803f80u);
   float psum = 0.f, rsum = 0.f;
 #pragma unroll
@@ -179,10 +184,14 @@ __device__ __forceinline__ void softmax_pack(const f32x16 (&s)[2], WaveState<D>&
   st.l_round += rsum;
 }
 
-template <int D, bool MASK>
+// EXT: sliding window and/or ALiBi.  The scores are first turned into log2-domain
+// logits x = s*c - slope2*|i - j| (slope2 = ALiBi slope * log2 e; base = i - j0 - 4hi,
+// so i - j = base - koff), masked on both sides (lo <= koff <= lim), then fed to
+// the same online softmax with unit scale.
+template <int D, bool MASK, bool EXT>
 __device__ __forceinline__ void process_tile(WaveState<D>& st, const uint8_t* kb, const uint8_t* vb,
                                              const int (&koff)[D / 16], const int (&voff)[D / 32], int lim,
-                                             int l32, float c) {
+                                             int l32, float c, int lo = 0, float base = 0.f, float slope2 = 0.f) {
   using LY = Lay<D>;
   constexpr int KK = D / 16;
   constexpr int DB = D / 32;
@@ -210,10 +219,24 @@ __device__ __forceinline__ void process_tile(WaveState<D>& st, const uint8_t* kb
   __builtin_amdgcn_sched_group_barrier(0x008, kPrefetch, 0);
 
   // ---- online softmax
-  const float mt = tile_rowmax<MASK>(sc, lim, c);
-  maybe_rescale<D>(st, mt);
   bf16x8 pb[2][2];
-  softmax_pack<D>(sc, st, c, pb);
+  if constexpr (EXT) {
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int kofs = a * 32 + 8 * (r >> 2) + (r & 3);
+        const float x = __builtin_fmaf(sc[a][r], c, -slope2 * fabsf(base - (float)kofs));
+        sc[a][r] = (!MASK || (kofs <= lim && kofs >= lo)) ? x : -INFINITY;
+      }
+    const float mt = tile_rowmax<false>(sc, 0, 1.f);
+    maybe_rescale<D, true>(st, mt);
+    softmax_pack<D, true>(sc, st, 1.f, pb);
+  } else {
+    const float mt = tile_rowmax<MASK>(sc, lim, c);
+    maybe_rescale<D>(st, mt);
+    softmax_pack<D>(sc, st, c, pb);
+  }
 
   // ---- O^T += V^T P^T.  V^T fragment for (a, h2, db): keys a*32 + h2*16 + 4*hi +
   // {0..3, 8..11}, d = db*32 + l32, via two transposing reads of 4 keys each
@@ -267,11 +290,12 @@ __device__ __forceinline__ void copy_tile(uint8_t* smem, const void* kbase, cons
   }
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool EXT>
 __global__ __launch_bounds__(kThreads, 8 / kWaves) void fwd_bf16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     uint16_t* __restrict__ O, float* __restrict__ Lse, int B, int Hq, int Hkv, int N,
-    float c /* |scale| * log2(e), > 0 */, uint32_t qsign /* 0x80008000 if scale < 0 */) {
+    float c /* |scale| * log2(e), > 0 */, uint32_t qsign /* 0x80008000 if scale < 0 */,
+    int window /* EXT: keys j >= i - window + 1 only (0: none) */, const float* __restrict__ slopes /* EXT: ALiBi */) {
   using LY = Lay<D>;
   constexpr int KK = D / 16;
   constexpr int DB = D / 32;
@@ -330,6 +354,9 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void fwd_bf16_kernel(
 
   const int kend = CAUSAL ? min(N, (qb + 1) * kBR) : N;
   const int ntiles = (kend + kBC - 1) / kBC;
+  // sliding window: tiles wholly left of the block's first row's window are never loaded
+  const int t_begin = (EXT && window > 0) ? max(0, qb * kBR - window + 1) / kBC : 0;
+  const float slope2 = (EXT && slopes != nullptr) ? slopes[h] * kLog2e : 0.f;
 
   // ---- HBM -> LDS copies of one K/V tile (buffer loads with the LDS bit).  Wave w
   // copies 1 KB blocks w, w + 8, ... of each tensor; lane l of a block writes
@@ -354,13 +381,13 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void fwd_bf16_kernel(
   constexpr int kLoadsPerTile = 2 * LY::BPW;
 #pragma unroll
   for (int p = 0; p < kStages - 1; ++p)
-    if (p < ntiles) copy_tile<D>(smem, kbase, vbase, head_bytes, kcp, vcp, p * kBC, p, w);
-  wait_vmem_tiles<kLoadsPerTile>(min(kStages - 2, ntiles - 1));  // tile 0 has landed
+    if (t_begin + p < ntiles) copy_tile<D>(smem, kbase, vbase, head_bytes, kcp, vcp, (t_begin + p) * kBC, p, w);
+  wait_vmem_tiles<kLoadsPerTile>(min(kStages - 2, ntiles - 1 - t_begin));  // the first tile has landed
   __syncthreads();
 
   // The loop is unrolled by kStages so every slot index, and with it every LDS
   // address offset, is a compile-time constant.
-  for (int t0 = 0; t0 < ntiles; t0 += kStages) {
+  for (int t0 = t_begin; t0 < ntiles; t0 += kStages) {
 #pragma unroll
     for (int u = 0; u < kStages; ++u) {
       const int t = t0 + u;
@@ -370,18 +397,30 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void fwd_bf16_kernel(
         copy_tile<D>(smem, kbase, vbase, head_bytes, kcp, vcp, j0 + (kStages - 1) * kBC, (u + kStages - 1) % kStages,
                      w);
 
-      const bool skip = CAUSAL && (j0 > rw0 + kRowsPerWave - 1);
+      const bool left_of_window = EXT && window > 0 && (j0 + kBC - 1 < rw0 - window + 1);
+      const bool skip = (CAUSAL && (j0 > rw0 + kRowsPerWave - 1)) || left_of_window;
       if (!skip) {
-        const bool need_mask = CAUSAL ? (j0 + kBC - 1 > rw0) : (j0 + kBC > N);
+        const bool need_mask = (CAUSAL ? (j0 + kBC - 1 > rw0) : (j0 + kBC > N)) ||
+                               (EXT && window > 0 && j0 < rw0 + kRowsPerWave - window);
         // causal: key j0 + koff visible iff koff + 4*hi <= qrow - j0 (keys past N
         // only reach rows >= N, which are never stored); otherwise iff key < N
         const int lim = (CAUSAL ? qrow - j0 : N - 1 - j0) - 4 * hi;
         const uint8_t* kb = smem + u * LY::TBYTES;
         const uint8_t* vb = smem + (kStages + u) * LY::TBYTES;
-        if (need_mask)
-          process_tile<D, true>(st, kb, vb, koff, voff, lim, l32, c);
-        else
-          process_tile<D, false>(st, kb, vb, koff, voff, lim, l32, c);
+        if constexpr (EXT) {
+          // window: key visible iff koff + 4*hi >= qrow - window + 1 - j0
+          const int lo = window > 0 ? qrow - window + 1 - j0 - 4 * hi : -kBC;
+          const float base = (float)(qrow - j0 - 4 * hi);
+          if (need_mask)
+            process_tile<D, true, true>(st, kb, vb, koff, voff, lim, l32, c, lo, base, slope2);
+          else
+            process_tile<D, false, true>(st, kb, vb, koff, voff, lim, l32, c, lo, base, slope2);
+        } else {
+          if (need_mask)
+            process_tile<D, true, false>(st, kb, vb, koff, voff, lim, l32, c);
+          else
+            process_tile<D, false, false>(st, kb, vb, koff, voff, lim, l32, c);
+        }
       }
 
       // tile t + 1 must have landed; the copies of later tiles may still be in flight
@@ -410,7 +449,7 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void fwd_bf16_kernel(
   }
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool EXT>
 hipError_t launch(const FwdArgs& a) {
   const int nqb = (a.N + kBR - 1) / kBR;
   const dim3 grid((unsigned)(nqb * a.B * a.Hq));
@@ -419,17 +458,21 @@ hipError_t launch(const FwdArgs& a) {
   float c = fabsf(a.scale) * kLog2e;
   if (!(c > 1e-30f)) c = 1e-30f;
   const uint32_t qsign = a.scale < 0.f ? 0x80008000u : 0u;
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL>), grid, dim3(kThreads), 0, (hipStream_t)a.stream,
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, EXT>), grid, dim3(kThreads), 0, (hipStream_t)a.stream,
                      (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o,
-                     a.lse, a.B, a.Hq, a.Hkv, a.N, c, qsign);
+                     a.lse, a.B, a.Hq, a.Hkv, a.N, c, qsign, a.window, a.slopes);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_fwd_bf16(const FwdArgs& a) {
-  if (a.d == 64) return a.causal ? launch<64, true>(a) : launch<64, false>(a);
-  return a.causal ? launch<128, true>(a) : launch<128, false>(a);
+  if (a.window > 0 || a.slopes != nullptr) {
+    if (a.d == 64) return a.causal ? launch<64, true, true>(a) : launch<64, false, true>(a);
+    return a.causal ? launch<128, true, true>(a) : launch<128, false, true>(a);
+  }
+  if (a.d == 64) return a.causal ? launch<64, true, false>(a) : launch<64, false, false>(a);
+  return a.causal ? launch<128, true, false>(a) : launch<128, false, false>(a);
 }
 
 }  // namespace fa

@@ -121,6 +121,12 @@ def make_prefill(B, Hq, Hkv, N, d, dtype="bf16", seed=0, value_scale=1.0):
     return {"q": q, "k": k, "v": v}
 
 
+def make_alibi_slopes(n_heads: int) -> torch.Tensor:
+    """fp32 ALiBi slopes 2^(-8 (h + 1) / n) for heads h = 0 .. n-1 (the geometric
+    sequence usually paired with the bias), as a CPU tensor."""
+    return torch.tensor([2.0 ** (-8.0 * (h + 1) / n_heads) for h in range(n_heads)], dtype=torch.float32)
+
+
 def make_grad_output(B, Hq, N, d, dtype="bf16", seed=0):
     """Upstream gradient dO [B, Hq, N, d] for the backward: N(0,1) from its own
     stream (seed + 7919, so it is independent of the forward inputs of the same seed)."""

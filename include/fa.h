@@ -83,6 +83,25 @@ int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* 
                void* stream);
 
 /*
+ * fa_fwd_ex -- fa_fwd with a sliding window and/or an ALiBi bias (bf16).
+ *
+ * Pages: "Phase 08", Lab 01 extensions row (sliding-window attention as in
+ * Mistral; ALiBi bias support).  Same tensors, layouts, outputs and status codes
+ * as fa_fwd, plus:
+ *   window        >= 0.  W > 0 keeps, for query i, only keys j >= i - W + 1 (the
+ *                 last W positions up to and including i); requires causal = 1
+ *                 (FA_ERR_UNSUPPORTED otherwise).  0: no window.
+ *   alibi_slopes  device pointer to Hq fp32 slopes m_h, or NULL for no bias; the
+ *                 score of (i, j) for query head h becomes
+ *                 scale * q_i . k_j - m_h * |i - j| (before masking), and lse is the
+ *                 logsumexp of these biased scores.  4-byte aligned.
+ * With window = 0 and alibi_slopes = NULL it computes exactly what fa_fwd does.
+ */
+int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
+              int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+              int window, const float* alibi_slopes, void* stream);
+
+/*
  * fa_bwd_workspace_size -- bytes of device workspace fa_bwd needs for these
  * sizes: D = rowsum(dO * O) per row (fp32), plus fp32 partial sums of dK and dV
  * when a K/V head's query heads are split over several workgroups (few K/V

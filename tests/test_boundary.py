@@ -32,7 +32,7 @@ def L():
 
 def test_every_declared_symbol_is_exported(L):
     names = declared_functions()
-    assert set(names) >= {"fa_fwd", "fa_fwd_f32", "fa_bwd", "fa_bwd_workspace_size", "fa_decode_paged",
+    assert set(names) >= {"fa_fwd", "fa_fwd_f32", "fa_fwd_ex", "fa_bwd", "fa_bwd_workspace_size", "fa_decode_paged",
                           "fa_decode_paged_workspace_size", "fa_status_string"}
     for n in names:
         assert hasattr(L, n), n
@@ -139,3 +139,19 @@ def test_bwd_workspace_size(L):
     assert fa.fa_bwd_workspace_size(2, 32, 1, 4096, 128) == dbytes(2, 32, 4096) + 2 * 8 * 2 * 1 * 4096 * 128 * 4
     assert fa.fa_bwd_workspace_size(1, 2, 1, 16, 96) == 0
     assert fa.fa_bwd_workspace_size(1, 3, 2, 16, 64) == 0
+
+
+def fwd_ex(L, window=0, slopes=Z, causal=1, **kw):
+    args = dict(q=P, k=P, v=P, o=P, lse=P, B=1, Hq=2, Hkv=1, N=16, d=64, scale=0.125)
+    args.update(kw)
+    return L.fa_fwd_ex(args["q"], args["k"], args["v"], args["o"], args["lse"], args["B"], args["Hq"], args["Hkv"],
+                       args["N"], args["d"], causal, args["scale"], window, slopes, Z)
+
+
+def test_fwd_ex_validation(L):
+    assert fwd_ex(L, window=-1) == SHAPE
+    assert fwd_ex(L, window=4, causal=0) == UNSUP
+    assert fwd_ex(L, slopes=ctypes.c_void_p(0x10002)) == ALIGN
+    assert fwd_ex(L, q=Z) == NULL
+    assert fwd_ex(L, d=80) == UNSUP
+    assert fwd_ex(L, window=3, q=Z, k=Z, v=Z, o=Z, lse=Z, N=0) == OK
