@@ -183,6 +183,17 @@ def make_decode(num_seqs, Hq, Hkv, d, ctx_lo=1, ctx_hi=64, seed=0, page_size=16,
     }
 
 
+def make_prefill_paged(num_seqs, Hq, Hkv, d, chunk, ctx_lo, ctx_hi, seed=0, page_size=16, fixed_ctx=(),
+                       dtype="bf16"):
+    """Chunked-prefill inputs over a paged cache: the paged K/V pools, page table and
+    ctx_lens of make_decode (context lengths drawn from [max(ctx_lo, chunk), ctx_hi]),
+    and chunk queries q [S, Hq, chunk, d] from their own stream (seed + 104729)."""
+    x = make_decode(num_seqs, Hq, Hkv, d, max(ctx_lo, chunk), ctx_hi, seed, page_size, None, fixed_ctx, dtype)
+    rng = np.random.default_rng(seed + 104729)
+    x["q"] = _to(_normal(rng, (num_seqs, Hq, chunk, d)), dtype)
+    return x
+
+
 def make_inputs(cfg):
     """Inputs for a registered configuration (PrefillConfig or DecodeConfig)."""
     if isinstance(cfg, str):

@@ -21,6 +21,7 @@ from .attention import (  # noqa: F401
     attention_ref,
     alibi_slopes_ref,
     decode_ref,
+    prefill_paged_ref,
     online_ref,
     lse_merge_ref,
     gather_pages_ref,

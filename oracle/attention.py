@@ -28,6 +28,7 @@ __all__ = [
     "attention_ref",
     "alibi_slopes_ref",
     "decode_ref",
+    "prefill_paged_ref",
     "online_ref",
     "lse_merge_ref",
     "gather_pages_ref",
@@ -167,6 +168,43 @@ def decode_ref(q, kpages, vpages, page_table, ctx_lens, scale: float):
             o, lse = _softmax_rows(sc, vs)
             O[s, hs] = o
             L[s, hs] = lse
+    return O, L
+
+
+def prefill_paged_ref(q, kpages, vpages, page_table, ctx_lens, scale: float):
+    """Chunked prefill over a paged KV cache, by the definition.
+
+    "Phase 08", Concepts list (chunked prefill: a long prompt is processed a chunk
+    at a time; paged attention) and Lab 03 steps 1 and 4 (16-token pages reached
+    through an indirection table).  Sequence s holds ctx_lens[s] cached tokens, the
+    last C of which are the chunk's own tokens (their K/V already written to the
+    cache); chunk row r is the token at position ctx_lens[s] - C + r and sees every
+    cached token at a position <= its own (causal within the chunk, everything
+    before it).  Requires ctx_lens[s] >= C.
+
+    q [S, Hq, C, d] -> O [S, Hq, C, d], L [S, Hq, C].
+    """
+    q = _f64(q)
+    S, Hq, C, d = q.shape
+    Hkv = np.asarray(kpages).shape[1]
+    G = _group_size(Hq, Hkv)
+    O = np.zeros((S, Hq, C, d))
+    L = np.zeros((S, Hq, C))
+    for s in range(S):
+        n = int(ctx_lens[s])
+        if n < C:
+            raise ValueError("every sequence must already hold its chunk (ctx_lens >= C)")
+        pos = n - C + np.arange(C)
+        keys = np.arange(n)
+        for g in range(Hkv):
+            ks = gather_pages_ref(kpages, page_table[s], n, g)
+            vs = gather_pages_ref(vpages, page_table[s], n, g)
+            for h in range(g * G, (g + 1) * G):
+                sc = scale * (q[s, h] @ ks.T)  # [C, n]
+                sc = np.where(keys[None, :] <= pos[:, None], sc, -np.inf)
+                o, lse = _softmax_rows(sc, vs)
+                O[s, h] = o
+                L[s, h] = lse
     return O, L
 
 

@@ -436,3 +436,61 @@ def test_alibi_slopes_are_the_geometric_sequence():
 def test_window_requires_causal():
     with pytest.raises(ValueError):
         attention_ref(np.zeros((1, 1, 2, 2)), np.zeros((1, 1, 2, 2)), np.zeros((1, 1, 2, 2)), False, 1.0, window=1)
+
+
+# ------------------------------------------------- chunked prefill over a paged cache
+
+from oracle import prefill_paged_ref  # noqa: E402
+from exact_io_aware_15_amd.workloads import make_prefill_paged  # noqa: E402
+
+
+def _paged(S, Hq, Hkv, d, C, ctx, seed):
+    x = make_prefill_paged(S, Hq, Hkv, d, C, 1, 64, seed=seed, fixed_ctx=ctx)
+    return (x["q"].double().numpy(), x["kpages"].double().numpy(), x["vpages"].double().numpy(),
+            x["page_table"].numpy(), x["ctx_lens"].numpy())
+
+
+def test_prefill_paged_chunk_of_one_is_decode():
+    q, kp, vp, pt, cl = _paged(3, 4, 2, 8, 1, (1, 17, 40), 80)
+    O, L = prefill_paged_ref(q, kp, vp, pt, cl, 0.3)
+    Od, Ld = decode_ref(q[:, :, 0], kp, vp, pt, cl, 0.3)
+    np.testing.assert_allclose(O[:, :, 0], Od, rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(L[:, :, 0], Ld, rtol=1e-13, atol=1e-13)
+
+
+def test_prefill_paged_whole_context_is_causal_prefill():
+    # ctx == C: the chunk is the whole sequence, i.e. a causal prefill of the gathered K/V
+    q, kp, vp, pt, cl = _paged(2, 4, 2, 8, 21, (21, 21), 81)
+    O, L = prefill_paged_ref(q, kp, vp, pt, cl, 0.4)
+    for s in range(2):
+        k = np.stack([gather_pages_ref(kp, pt[s], 21, g) for g in range(2)])[None]
+        v = np.stack([gather_pages_ref(vp, pt[s], 21, g) for g in range(2)])[None]
+        Oc, Lc = attention_ref(q[s][None], k, v, True, 0.4)
+        np.testing.assert_allclose(O[s], Oc[0], rtol=1e-13, atol=1e-13)
+        np.testing.assert_allclose(L[s], Lc[0], rtol=1e-13, atol=1e-13)
+
+
+def test_prefill_paged_matches_brute_force():
+    q, kp, vp, pt, cl = _paged(2, 2, 1, 3, 4, (6, 9), 82)
+    O, L = prefill_paged_ref(q, kp, vp, pt, cl, 0.7)
+    for s in range(2):
+        n = int(cl[s])
+        k = [[gather_pages_ref(kp, pt[s], n, 0).tolist()]]
+        v = [[gather_pages_ref(vp, pt[s], n, 0).tolist()]]
+        # the chunk rows are the last C rows of a causal attention over the whole sequence
+        qq = np.zeros((1, 2, n, 3))
+        qq[0, :, n - 4:] = q[s]
+        Ob, Lb = brute_attention(qq.tolist(), k, v, True, 0.7)
+        np.testing.assert_allclose(O[s], np.array(Ob)[0][:, n - 4:], rtol=1e-13, atol=1e-13)
+        np.testing.assert_allclose(L[s], np.array(Lb)[0][:, n - 4:], rtol=1e-13, atol=1e-13)
+
+
+def test_prefill_paged_ignores_page_order():
+    q, kp, vp, pt, cl = _paged(2, 2, 2, 8, 5, (33, 50), 83)
+    O, L = prefill_paged_ref(q, kp, vp, pt, cl, 0.5)
+    perm = np.random.default_rng(5).permutation(kp.shape[0])
+    inv = np.argsort(perm)
+    pt2 = np.where(pt < kp.shape[0], inv[pt], pt)
+    O2, L2 = prefill_paged_ref(q, kp[perm], vp[perm], pt2, cl, 0.5)
+    np.testing.assert_allclose(O, O2, rtol=0, atol=0)
+    np.testing.assert_allclose(L, L2, rtol=0, atol=0)
