@@ -444,14 +444,14 @@ from oracle import prefill_paged_ref  # noqa: E402
 from exact_io_aware_15_amd.workloads import make_prefill_paged  # noqa: E402
 
 
-def _paged(S, Hq, Hkv, d, C, ctx, seed):
+def _chunked(S, Hq, Hkv, d, C, ctx, seed):
     x = make_prefill_paged(S, Hq, Hkv, d, C, 1, 64, seed=seed, fixed_ctx=ctx)
     return (x["q"].double().numpy(), x["kpages"].double().numpy(), x["vpages"].double().numpy(),
             x["page_table"].numpy(), x["ctx_lens"].numpy())
 
 
 def test_prefill_paged_chunk_of_one_is_decode():
-    q, kp, vp, pt, cl = _paged(3, 4, 2, 8, 1, (1, 17, 40), 80)
+    q, kp, vp, pt, cl = _chunked(3, 4, 2, 8, 1, (1, 17, 40), 80)
     O, L = prefill_paged_ref(q, kp, vp, pt, cl, 0.3)
     Od, Ld = decode_ref(q[:, :, 0], kp, vp, pt, cl, 0.3)
     np.testing.assert_allclose(O[:, :, 0], Od, rtol=1e-13, atol=1e-13)
@@ -460,7 +460,7 @@ def test_prefill_paged_chunk_of_one_is_decode():
 
 def test_prefill_paged_whole_context_is_causal_prefill():
     # ctx == C: the chunk is the whole sequence, i.e. a causal prefill of the gathered K/V
-    q, kp, vp, pt, cl = _paged(2, 4, 2, 8, 21, (21, 21), 81)
+    q, kp, vp, pt, cl = _chunked(2, 4, 2, 8, 21, (21, 21), 81)
     O, L = prefill_paged_ref(q, kp, vp, pt, cl, 0.4)
     for s in range(2):
         k = np.stack([gather_pages_ref(kp, pt[s], 21, g) for g in range(2)])[None]
@@ -471,7 +471,7 @@ def test_prefill_paged_whole_context_is_causal_prefill():
 
 
 def test_prefill_paged_matches_brute_force():
-    q, kp, vp, pt, cl = _paged(2, 2, 1, 3, 4, (6, 9), 82)
+    q, kp, vp, pt, cl = _chunked(2, 2, 1, 3, 4, (6, 9), 82)
     O, L = prefill_paged_ref(q, kp, vp, pt, cl, 0.7)
     for s in range(2):
         n = int(cl[s])
@@ -486,7 +486,7 @@ def test_prefill_paged_matches_brute_force():
 
 
 def test_prefill_paged_ignores_page_order():
-    q, kp, vp, pt, cl = _paged(2, 2, 2, 8, 5, (33, 50), 83)
+    q, kp, vp, pt, cl = _chunked(2, 2, 2, 8, 5, (33, 50), 83)
     O, L = prefill_paged_ref(q, kp, vp, pt, cl, 0.5)
     perm = np.random.default_rng(5).permutation(kp.shape[0])
     inv = np.argsort(perm)
