@@ -163,6 +163,8 @@ def main():
                     help="oracle baseline on the first n sequences of the decode (64 = the whole workload)")
     ap.add_argument("--only", choices=["prefill", "decode", "backward"], default=None,
                     help="time one part only (for profiling runs)")
+    ap.add_argument("--no-chunked", action="store_true",
+                    help="skip the chunked paged-prefill measurement (reported beside the step)")
     ap.add_argument("--no-window", action="store_true",
                     help="skip the sliding-window + ALiBi measurement (reported beside the step)")
     ap.add_argument("--no-bwd", action="store_true",
@@ -324,6 +326,42 @@ def main():
               "workload": f"causal bf16 prefill B1 Hq32 N8192 d128 with a {W}-key sliding window and ALiBi "
                           "slopes 2^(-8(h+1)/32); FLOPs over visible pairs only"}
 
+    cp = None
+    if run_b and not args.no_chunked:
+        # chunked prefill over a paged cache (not part of the step): 16 sequences, 512-token
+        # chunks, contexts U[512, 16384], Hq32 Hkv8 d128; FLOPs over the visible pairs
+        from exact_io_aware_15_amd.workloads import make_prefill_paged
+        cx = make_prefill_paged(16, 32, 8, 128, 512, 512, 16384, seed=6)
+        cg = {kk: (vv.to(dev) if torch.is_tensor(vv) else vv) for kk, vv in cx.items()}
+        co = torch.empty_like(cg["q"])
+        cl = torch.empty(cg["q"].shape[:3], dtype=torch.float32, device=dev)
+
+        def chunked():
+            fa.fa_prefill_paged(cg["q"], cg["kpages"], cg["vpages"], cg["page_table"], cg["ctx_lens"], out=co,
+                                lse=cl)
+
+        for _ in range(max(1, args.warmup // 3)):
+            chunked()
+        torch.cuda.synchronize()
+        cev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
+        for i in range(K):
+            cev[i][0].record()
+            chunked()
+            cev[i][1].record()
+        torch.cuda.synchronize()
+        c_ms = sum(e[0].elapsed_time(e[1]) for e in cev) / K
+        ctxs = cx["ctx_lens"].long()
+        pairs = int((512 * (ctxs - 512) + 512 * 513 // 2).sum())
+        cfl = 4.0 * 32 * 128 * pairs
+        ctf = cfl / (c_ms * 1e-3) / 1e12
+        log(f"chunked prefill {c_ms:.4f} ms ({ctf:.1f} TFLOP/s)")
+        cp = {"value": round(ctf, 2), "unit": "TFLOP/s", "ms": round(c_ms, 5),
+              "roofline": {"bound": "mfma", "achieved": round(ctf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                           "frac": round(ctf / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                           "kernel": "fwd_bf16_kernel<128, causal, paged>", "algorithmic_flops_per_launch": cfl},
+              "workload": "chunked prefill over 16-token pages: 16 sequences x 512-token chunks, contexts "
+                          f"U[512,16384] (total {int(ctxs.sum())}), Hq32 Hkv8 d128; FLOPs over visible pairs"}
+
     res = {"metric": METRIC, "n_gpus": 1, "steps": K, "warmup": args.warmup, "ms_per_step": round(step_ms, 5),
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
            "data": "synthetic (seeded N(0,1) inputs; random page permutation)"}
@@ -356,6 +394,8 @@ def main():
             res.update({"value": dec["value"], "unit": "GB/s", "roofline": dec["roofline"]})
     if wa is not None:
         res["window_alibi"] = wa
+    if cp is not None:
+        res["chunked_prefill"] = cp
     if bwd is not None:
         res["backward"] = bwd
         if not run_p and not run_d:

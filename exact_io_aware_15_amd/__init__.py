@@ -26,6 +26,7 @@ __all__ = [
     "fa_bwd_workspace_size",
     "fa_decode_paged",
     "fa_decode_paged_workspace_size",
+    "fa_prefill_paged",
     "fa_status_string",
     "LIB_PATH",
 ]
@@ -61,6 +62,8 @@ def lib() -> ctypes.CDLL:
     L.fa_bwd_workspace_size.restype = sz
     L.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp, sz, vp]
     L.fa_bwd.restype = i
+    L.fa_prefill_paged.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, f, vp]
+    L.fa_prefill_paged.restype = i
     L.fa_decode_paged_workspace_size.argtypes = [i, i, i, i, i]
     L.fa_decode_paged_workspace_size.restype = sz
     L.fa_decode_paged.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp, sz, vp]
@@ -229,4 +232,32 @@ def fa_decode_paged(q, kpages, vpages, page_table, ctx_lens, scale=None, out=Non
                                _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(q))
     if st != FA_OK:
         raise FAError(st, "fa_decode_paged")
+    return out, lse
+
+
+def fa_prefill_paged(q, kpages, vpages, page_table, ctx_lens, scale=None, out=None, lse=None):
+    """Chunked prefill: q [S,Hq,C,d] bf16 (the last C tokens of each sequence's cache);
+    kpages/vpages [P,Hkv,16,d] bf16; page_table [S,maxp] int32; ctx_lens [S] int32 (>= C)
+    -> (O bf16 [S,Hq,C,d], L fp32 [S,Hq,C])."""
+    S, Hq, C, d = q.shape
+    P, Hkv, page_size, _ = kpages.shape
+    maxp = page_table.shape[1]
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on a GPU")
+    _need(q, "q", torch.bfloat16, (S, Hq, C, d), dev)
+    _need(kpages, "kpages", torch.bfloat16, (P, Hkv, page_size, d), dev)
+    _need(vpages, "vpages", torch.bfloat16, (P, Hkv, page_size, d), dev)
+    _need(page_table, "page_table", torch.int32, (S, maxp), dev)
+    _need(ctx_lens, "ctx_lens", torch.int32, (S,), dev)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    out = torch.empty((S, Hq, C, d), dtype=torch.bfloat16, device=dev) if out is None else out
+    lse = torch.empty((S, Hq, C), dtype=torch.float32, device=dev) if lse is None else lse
+    _need(out, "out", torch.bfloat16, (S, Hq, C, d), dev)
+    _need(lse, "lse", torch.float32, (S, Hq, C), dev)
+    st = lib().fa_prefill_paged(_ptr(q), _ptr(kpages), _ptr(vpages), _ptr(page_table), _ptr(ctx_lens), _ptr(out),
+                                _ptr(lse), S, Hq, Hkv, d, C, page_size, maxp, P, float(scale), _stream(q))
+    if st != FA_OK:
+        raise FAError(st, "fa_prefill_paged")
     return out, lse

@@ -82,6 +82,27 @@ int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, 
   return finish(fa::launch_fwd_bf16(a), stream);
 }
 
+int fa_prefill_paged(const void* q, const void* kpages, const void* vpages, const int32_t* page_table,
+                     const int32_t* ctx_lens, void* o, float* lse, int num_seqs, int Hq, int Hkv, int d, int chunk,
+                     int page_size, int max_pages_per_seq, int num_pages, float scale, void* stream) {
+  if (num_seqs < 0 || chunk < 0 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || max_pages_per_seq < 1 || num_pages < 1)
+    return FA_ERR_SHAPE;
+  if ((long long)num_seqs * Hq * ((chunk + 255) / 256) > 0x7fffffffLL) return FA_ERR_SHAPE;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  if (page_size != 16) return FA_ERR_UNSUPPORTED;
+  if (!std::isfinite(scale)) return FA_ERR_SCALE;
+  if (num_seqs == 0 || chunk == 0) return FA_OK;
+  if (!q || !kpages || !vpages || !page_table || !ctx_lens || !o || !lse) return FA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(kpages) || !aligned16(vpages) || !aligned16(page_table) ||
+      !aligned16(ctx_lens) || !aligned16(o) || !aligned16(lse))
+    return FA_ERR_ALIGN;
+  fa::FwdArgs a{q, kpages, vpages, o, lse, num_seqs, Hq, Hkv, chunk, d, true, scale, stream};
+  a.page_table = page_table;
+  a.ctx_lens = ctx_lens;
+  a.max_pages = max_pages_per_seq;
+  return finish(fa::launch_prefill_paged(a), stream);
+}
+
 size_t fa_bwd_workspace_size(int B, int Hq, int Hkv, int N, int d) {
   if (B < 0 || N < 0 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || (d != 64 && d != 128)) return 0;
   return fa::bwd_plan(B, Hq, Hkv, N, d).bytes;

@@ -20,6 +20,11 @@ struct FwdArgs {
   void* stream;
   int window = 0;                 // bf16 only: keys j >= i - window + 1 (0: none)
   const float* slopes = nullptr;  // bf16 only: ALiBi slope per query head, or none
+  // chunked prefill over a paged cache (launch_prefill_paged): B = sequences, N = chunk
+  // length, k/v = page pools [pages][Hkv][16][d]
+  const int32_t* page_table = nullptr;
+  const int32_t* ctx_lens = nullptr;
+  int max_pages = 0;
 };
 
 struct DecodeArgs {
@@ -96,6 +101,7 @@ inline BwdPlan bwd_plan(int B, int Hq, int Hkv, int N, int d) {
 }
 
 hipError_t launch_fwd_bf16(const FwdArgs& a);
+hipError_t launch_prefill_paged(const FwdArgs& a);
 hipError_t launch_bwd_bf16(const BwdArgs& a);
 hipError_t launch_fwd_f32(const FwdArgs& a);
 hipError_t launch_decode_paged(const DecodeArgs& a);

@@ -290,12 +290,51 @@ __device__ __forceinline__ void copy_tile(uint8_t* smem, const void* kbase, cons
   }
 }
 
-template <int D, bool CAUSAL, bool EXT>
+// PAGED: chunked prefill over a paged cache.  B counts sequences and N is the
+// chunk length C; sequence s holds ctxl[s] >= C cached tokens in 16-token pages
+// (K, V are the page pools [pages][Hkv][16][D], table the page table), the chunk
+// rows sit at positions ctxl[s] - C + r and the attention is causal in positions.
+// HBM -> LDS copy of one K/V tile (keys j0 .. j0+63, four 16-token pages) from the
+// page pools, into buffer buf with the same swizzled layout as copy_tile.  Each 1 KB
+// block lies in one page (slot rows pr0 .. pr0 + RPB - 1); its buffer descriptor
+// spans only the page's valid slots (below nk), so slots past the context -- and
+// whole pages past it, whose table entries are never read -- land as zeros.
+template <int D>
+__device__ __forceinline__ void copy_tile_paged(uint8_t* smem, const uint16_t* kpool, const uint16_t* vpool,
+                                                const int32_t* trow, int nk, int Hkv, int g, int j0, int buf, int w,
+                                                int lane) {
+  using LY = Lay<D>;
+  uint8_t* kb = smem + buf * LY::TBYTES;
+  uint8_t* vb = smem + (kStages + buf) * LY::TBYTES;
+#pragma unroll
+  for (int i = 0; i < LY::BPW; ++i) {
+    const int blk = w + kWaves * i;
+    const int r0 = blk * LY::RPB;                 // tile row of the block's first row
+    const int tp = (j0 + r0) / 16;                // logical page
+    const int valid = min(max(nk - tp * 16, 0), 16);
+    const int pid = valid > 0 ? trow[tp] : 0;
+    const size_t head = ((size_t)pid * Hkv + g) * 16 * D;
+    const auto krs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(kpool + head), (short)0,
+                                                       (uint32_t)valid * LY::ROWB, 0x00020000);
+    const auto vrs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(vpool + head), (short)0,
+                                                       (uint32_t)valid * LY::ROWB, 0x00020000);
+    const int r = r0 + lane / LY::CPR;            // tile row this lane copies
+    const int pc = lane % LY::CPR;
+    const uint32_t ko = (r % 16) * LY::ROWB + ((pc ^ LY::swz_k(r)) << 4);
+    const uint32_t vo = (r % 16) * LY::ROWB + ((pc ^ LY::swz_v(r)) << 4);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (FA_LDS void*)(kb + blk * 1024), 16, ko, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (FA_LDS void*)(vb + blk * 1024), 16, vo, 0, 0, 0);
+  }
+}
+
+template <int D, bool CAUSAL, bool EXT, bool PAGED>
 __global__ __launch_bounds__(kThreads, 8 / kWaves) void fwd_bf16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     uint16_t* __restrict__ O, float* __restrict__ Lse, int B, int Hq, int Hkv, int N,
     float c /* |scale| * log2(e), > 0 */, uint32_t qsign /* 0x80008000 if scale < 0 */,
-    int window /* EXT: keys j >= i - window + 1 only (0: none) */, const float* __restrict__ slopes /* EXT: ALiBi */) {
+    int window /* EXT: keys j >= i - window + 1 only (0: none) */, const float* __restrict__ slopes /* EXT: ALiBi */,
+    const int32_t* __restrict__ table /* PAGED */, const int32_t* __restrict__ ctxl /* PAGED */,
+    int max_pages /* PAGED */) {
   using LY = Lay<D>;
   constexpr int KK = D / 16;
   constexpr int DB = D / 32;
@@ -319,8 +358,14 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void fwd_bf16_kernel(
   const int qrow = rw0 + l32;
 
   const uint16_t* qbase = Q + ((size_t)(b * Hq + h) * N) * D;
-  const uint16_t* kbase = K + ((size_t)(b * Hkv + g) * N) * D;
-  const uint16_t* vbase = V + ((size_t)(b * Hkv + g) * N) * D;
+  const uint16_t* kbase = K + (PAGED ? 0 : ((size_t)(b * Hkv + g) * N) * D);
+  const uint16_t* vbase = V + (PAGED ? 0 : ((size_t)(b * Hkv + g) * N) * D);
+  // keys and the position of query row 0 (the chunk's first token when paged)
+  const int Nk = PAGED ? ctxl[b] : N;
+  const int poff = PAGED ? Nk - N : 0;
+  const int rw0p = rw0 + poff;
+  const int qrowp = qrow + poff;
+  const int32_t* trow = PAGED ? table + (size_t)b * max_pages : nullptr;
 
   WaveState<D> st;
   // Q fragments (B operand of S^T = K Q^T): row qrow, d = kk*16 + hi*8 .. +8
@@ -352,10 +397,10 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void fwd_bf16_kernel(
     }
   }
 
-  const int kend = CAUSAL ? min(N, (qb + 1) * kBR) : N;
+  const int kend = CAUSAL ? min(Nk, poff + (qb + 1) * kBR) : Nk;
   const int ntiles = (kend + kBC - 1) / kBC;
   // sliding window: tiles wholly left of the block's first row's window are never loaded
-  const int t_begin = (EXT && window > 0) ? max(0, qb * kBR - window + 1) / kBC : 0;
+  const int t_begin = (EXT && window > 0) ? max(0, poff + qb * kBR - window + 1) / kBC : 0;
   const float slope2 = (EXT && slopes != nullptr) ? slopes[h] * kLog2e : 0.f;
 
   // ---- HBM -> LDS copies of one K/V tile (buffer loads with the LDS bit).  Wave w
@@ -381,7 +426,12 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void fwd_bf16_kernel(
   constexpr int kLoadsPerTile = 2 * LY::BPW;
 #pragma unroll
   for (int p = 0; p < kStages - 1; ++p)
-    if (t_begin + p < ntiles) copy_tile<D>(smem, kbase, vbase, head_bytes, kcp, vcp, (t_begin + p) * kBC, p, w);
+    if (t_begin + p < ntiles) {
+      if constexpr (PAGED)
+        copy_tile_paged<D>(smem, K, V, trow, Nk, Hkv, g, (t_begin + p) * kBC, p, w, lane);
+      else
+        copy_tile<D>(smem, kbase, vbase, head_bytes, kcp, vcp, (t_begin + p) * kBC, p, w);
+    }
   wait_vmem_tiles<kLoadsPerTile>(min(kStages - 2, ntiles - 1 - t_begin));  // the first tile has landed
   __syncthreads();
 
@@ -393,24 +443,29 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void fwd_bf16_kernel(
       const int t = t0 + u;
       if (t >= ntiles) break;
       const int j0 = t * kBC;
-      if (t + kStages - 1 < ntiles)
-        copy_tile<D>(smem, kbase, vbase, head_bytes, kcp, vcp, j0 + (kStages - 1) * kBC, (u + kStages - 1) % kStages,
-                     w);
+      if (t + kStages - 1 < ntiles) {
+        if constexpr (PAGED)
+          copy_tile_paged<D>(smem, K, V, trow, Nk, Hkv, g, j0 + (kStages - 1) * kBC, (u + kStages - 1) % kStages, w,
+                             lane);
+        else
+          copy_tile<D>(smem, kbase, vbase, head_bytes, kcp, vcp, j0 + (kStages - 1) * kBC,
+                       (u + kStages - 1) % kStages, w);
+      }
 
-      const bool left_of_window = EXT && window > 0 && (j0 + kBC - 1 < rw0 - window + 1);
-      const bool skip = (CAUSAL && (j0 > rw0 + kRowsPerWave - 1)) || left_of_window;
+      const bool left_of_window = EXT && window > 0 && (j0 + kBC - 1 < rw0p - window + 1);
+      const bool skip = (CAUSAL && (j0 > rw0p + kRowsPerWave - 1)) || left_of_window;
       if (!skip) {
-        const bool need_mask = (CAUSAL ? (j0 + kBC - 1 > rw0) : (j0 + kBC > N)) ||
-                               (EXT && window > 0 && j0 < rw0 + kRowsPerWave - window);
+        const bool need_mask = (CAUSAL ? (j0 + kBC - 1 > rw0p) : (j0 + kBC > Nk)) ||
+                               (EXT && window > 0 && j0 < rw0p + kRowsPerWave - window);
         // causal: key j0 + koff visible iff koff + 4*hi <= qrow - j0 (keys past N
         // only reach rows >= N, which are never stored); otherwise iff key < N
-        const int lim = (CAUSAL ? qrow - j0 : N - 1 - j0) - 4 * hi;
+        const int lim = (CAUSAL ? qrowp - j0 : Nk - 1 - j0) - 4 * hi;
         const uint8_t* kb = smem + u * LY::TBYTES;
         const uint8_t* vb = smem + (kStages + u) * LY::TBYTES;
         if constexpr (EXT) {
           // window: key visible iff koff + 4*hi >= qrow - window + 1 - j0
-          const int lo = window > 0 ? qrow - window + 1 - j0 - 4 * hi : -kBC;
-          const float base = (float)(qrow - j0 - 4 * hi);
+          const int lo = window > 0 ? qrowp - window + 1 - j0 - 4 * hi : -kBC;
+          const float base = (float)(qrowp - j0 - 4 * hi);
           if (need_mask)
             process_tile<D, true, true>(st, kb, vb, koff, voff, lim, l32, c, lo, base, slope2);
           else
@@ -449,7 +504,7 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void fwd_bf16_kernel(
   }
 }
 
-template <int D, bool CAUSAL, bool EXT>
+template <int D, bool CAUSAL, bool EXT, bool PAGED = false>
 hipError_t launch(const FwdArgs& a) {
   const int nqb = (a.N + kBR - 1) / kBR;
   const dim3 grid((unsigned)(nqb * a.B * a.Hq));
@@ -458,13 +513,18 @@ hipError_t launch(const FwdArgs& a) {
   float c = fabsf(a.scale) * kLog2e;
   if (!(c > 1e-30f)) c = 1e-30f;
   const uint32_t qsign = a.scale < 0.f ? 0x80008000u : 0u;
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, EXT>), grid, dim3(kThreads), 0, (hipStream_t)a.stream,
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, EXT, PAGED>), grid, dim3(kThreads), 0, (hipStream_t)a.stream,
                      (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o,
-                     a.lse, a.B, a.Hq, a.Hkv, a.N, c, qsign, a.window, a.slopes);
+                     a.lse, a.B, a.Hq, a.Hkv, a.N, c, qsign, a.window, a.slopes, a.page_table, a.ctx_lens,
+                     a.max_pages);
   return hipGetLastError();
 }
 
 }  // namespace
+
+hipError_t launch_prefill_paged(const FwdArgs& a) {
+  return a.d == 64 ? launch<64, true, false, true>(a) : launch<128, true, false, true>(a);
+}
 
 hipError_t launch_fwd_bf16(const FwdArgs& a) {
   if (a.window > 0 || a.slopes != nullptr) {

@@ -102,6 +102,32 @@ int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
               int window, const float* alibi_slopes, void* stream);
 
 /*
+ * fa_prefill_paged -- chunked prefill: a chunk of `chunk` new query tokens per
+ * sequence attends to the sequence's paged KV cache, causal within the chunk.
+ *
+ * Pages: "Phase 08", Concepts (chunked prefill splits a long prompt into pieces;
+ * paged attention) and Lab 03 steps 1 and 4 (16-token pages behind an
+ * indirection table).  Sequence s holds ctx_lens[s] cached tokens whose last
+ * `chunk` are the chunk's own (their K/V already written to the cache); chunk row
+ * r is the token at position ctx_lens[s] - chunk + r and sees every cached token
+ * at a position <= its own.
+ *
+ *   q          [S, Hq, chunk, d] bf16         o   [S, Hq, chunk, d] bf16 (out)
+ *   lse        [S, Hq, chunk] fp32 (out, natural-log logsumexp)
+ *   kpages, vpages, page_table, num_pages, max_pages_per_seq: as fa_decode_paged.
+ *   ctx_lens   [S] int32, chunk <= ctx_lens[s] <= max_pages_per_seq * page_size
+ *              (device data, trusted).  Cache slots at or beyond ctx_lens[s] never
+ *              affect the result, whatever they hold.
+ *   d in {64, 128}; page_size == 16; Hq % Hkv == 0; any finite scale.  No
+ *   workspace.  S = 0 or chunk = 0 is a no-op.
+ */
+int fa_prefill_paged(const void* q, const void* kpages, const void* vpages,
+                     const int32_t* page_table, const int32_t* ctx_lens,
+                     void* o, float* lse, int num_seqs, int Hq, int Hkv, int d,
+                     int chunk, int page_size, int max_pages_per_seq,
+                     int num_pages, float scale, void* stream);
+
+/*
  * fa_bwd_workspace_size -- bytes of device workspace fa_bwd needs for these
  * sizes: D = rowsum(dO * O) per row (fp32), plus fp32 partial sums of dK and dV
  * when a K/V head's query heads are split over several workgroups (few K/V

@@ -32,7 +32,7 @@ def L():
 
 def test_every_declared_symbol_is_exported(L):
     names = declared_functions()
-    assert set(names) >= {"fa_fwd", "fa_fwd_f32", "fa_fwd_ex", "fa_bwd", "fa_bwd_workspace_size", "fa_decode_paged",
+    assert set(names) >= {"fa_fwd", "fa_fwd_f32", "fa_fwd_ex", "fa_prefill_paged", "fa_bwd", "fa_bwd_workspace_size", "fa_decode_paged",
                           "fa_decode_paged_workspace_size", "fa_status_string"}
     for n in names:
         assert hasattr(L, n), n
@@ -155,3 +155,20 @@ def test_fwd_ex_validation(L):
     assert fwd_ex(L, q=Z) == NULL
     assert fwd_ex(L, d=80) == UNSUP
     assert fwd_ex(L, window=3, q=Z, k=Z, v=Z, o=Z, lse=Z, N=0) == OK
+
+
+def pp(L, q=P, kp=P, vp=P, pt=P, cl=P, o=P, lse=P, S=2, Hq=8, Hkv=2, d=128, C=5, ps=16, maxp=4, npages=9,
+       scale=0.1):
+    return L.fa_prefill_paged(q, kp, vp, pt, cl, o, lse, S, Hq, Hkv, d, C, ps, maxp, npages, scale, Z)
+
+
+def test_prefill_paged_validation(L):
+    assert pp(L, cl=Z) == NULL
+    assert pp(L, d=96) == UNSUP
+    assert pp(L, ps=8) == UNSUP
+    assert pp(L, Hq=6, Hkv=4) == SHAPE
+    assert pp(L, C=-1) == SHAPE
+    assert pp(L, scale=float("nan")) == SCALE
+    assert pp(L, o=MIS) == ALIGN
+    assert pp(L, q=Z, kp=Z, vp=Z, pt=Z, cl=Z, o=Z, lse=Z, C=0) == OK
+    assert pp(L, q=Z, kp=Z, vp=Z, pt=Z, cl=Z, o=Z, lse=Z, S=0) == OK
