@@ -194,6 +194,30 @@ def make_prefill_paged(num_seqs, Hq, Hkv, d, chunk, ctx_lo, ctx_hi, seed=0, page
     return x
 
 
+def make_decode_int8(num_seqs, Hq, Hkv, d, ctx_lo=1, ctx_hi=64, seed=0, page_size=16, fixed_ctx=(),
+                     group=32):
+    """Paged decode inputs with an INT8 group-scaled KV cache: the q, page table and
+    ctx_lens of make_decode (same seed), K/V pools [P+1, Hkv, page, d] int8 uniform in
+    [-127, 127] and fp32 scales [P+1, Hkv, page, d // group] uniform in [1/256, 1/64]
+    (so K/V values are O(1)).  Slots past each context and the padding page have NaN
+    scales, which a kernel must never let through."""
+    x = make_decode(num_seqs, Hq, Hkv, d, ctx_lo, ctx_hi, seed, page_size, None, fixed_ctx)
+    P1 = x["num_pages"]
+    rng = np.random.default_rng(seed + 15485863)
+    kq = rng.integers(-127, 128, size=(P1, Hkv, page_size, d), dtype=np.int64).astype(np.int8)
+    vq = rng.integers(-127, 128, size=(P1, Hkv, page_size, d), dtype=np.int64).astype(np.int8)
+    ks = rng.uniform(1 / 256, 1 / 64, size=(P1, Hkv, page_size, d // group)).astype(np.float32)
+    vs = rng.uniform(1 / 256, 1 / 64, size=(P1, Hkv, page_size, d // group)).astype(np.float32)
+    # NaN scales wherever the bf16 pools of make_decode hold NaN (unused slots, padding page)
+    bad = torch.isnan(x["kpages"][..., 0]).numpy()
+    ks[bad] = np.nan
+    vs[bad] = np.nan
+    x.update({"kq": torch.from_numpy(kq), "vq": torch.from_numpy(vq), "kscale": torch.from_numpy(ks),
+              "vscale": torch.from_numpy(vs), "group": group})
+    del x["kpages"], x["vpages"]
+    return x
+
+
 def make_inputs(cfg):
     """Inputs for a registered configuration (PrefillConfig or DecodeConfig)."""
     if isinstance(cfg, str):

@@ -22,6 +22,8 @@ from .attention import (  # noqa: F401
     alibi_slopes_ref,
     decode_ref,
     prefill_paged_ref,
+    dequant_pages_ref,
+    decode_int8_ref,
     online_ref,
     lse_merge_ref,
     gather_pages_ref,

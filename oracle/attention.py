@@ -29,6 +29,8 @@ __all__ = [
     "alibi_slopes_ref",
     "decode_ref",
     "prefill_paged_ref",
+    "dequant_pages_ref",
+    "decode_int8_ref",
     "online_ref",
     "lse_merge_ref",
     "gather_pages_ref",
@@ -169,6 +171,24 @@ def decode_ref(q, kpages, vpages, page_table, ctx_lens, scale: float):
             O[s, hs] = o
             L[s, hs] = lse
     return O, L
+
+
+def dequant_pages_ref(qpages, scales, group: int):
+    """fp64 values of group-scaled int8 pages: qpages [P, Hkv, page, d] int8 times
+    scales [P, Hkv, page, d // group] (one scale per token and `group` consecutive
+    channels).  screna.ai KV-cache quantization block (INT8 KV cache; group-wise
+    scales)."""
+    qv = _f64(qpages)
+    sc = np.repeat(_f64(scales), group, axis=-1)
+    return qv * sc
+
+
+def decode_int8_ref(q, kq, kscale, vq, vscale, page_table, ctx_lens, scale: float, group: int = 32):
+    """Paged decode over an INT8 group-scaled KV cache: the decode definition applied
+    to the dequantized cache (screna.ai KV-cache quantization block; "Phase 08" Lab 03
+    step 4)."""
+    return decode_ref(q, dequant_pages_ref(kq, kscale, group), dequant_pages_ref(vq, vscale, group), page_table,
+                      ctx_lens, scale)
 
 
 def prefill_paged_ref(q, kpages, vpages, page_table, ctx_lens, scale: float):
