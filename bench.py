@@ -163,6 +163,8 @@ def main():
                     help="oracle baseline on the first n sequences of the decode (64 = the whole workload)")
     ap.add_argument("--only", choices=["prefill", "decode", "backward"], default=None,
                     help="time one part only (for profiling runs)")
+    ap.add_argument("--no-int8", action="store_true",
+                    help="skip the INT8-cache decode measurement (reported beside the step)")
     ap.add_argument("--no-chunked", action="store_true",
                     help="skip the chunked paged-prefill measurement (reported beside the step)")
     ap.add_argument("--no-window", action="store_true",
@@ -362,6 +364,47 @@ def main():
               "workload": "chunked prefill over 16-token pages: 16 sequences x 512-token chunks, contexts "
                           f"U[512,16384] (total {int(ctxs.sum())}), Hq32 Hkv8 d128; FLOPs over visible pairs"}
 
+    d8 = None
+    if run_b and not args.no_int8:
+        # INT8 group-scaled paged decode on the decode workload's shapes and seed (not part
+        # of the step); algorithmic bytes: int8 K/V and their fp32 scales of every valid
+        # token, plus q, O, L, the used page-table entries and ctx_lens
+        from exact_io_aware_15_amd.workloads import make_decode_int8
+        ix = make_decode_int8(dcfg.num_seqs, dcfg.Hq, dcfg.Hkv, dcfg.d, dcfg.ctx_lo, dcfg.ctx_hi, dcfg.seed)
+        ig = {kk: (vv.to(dev) if torch.is_tensor(vv) else vv) for kk, vv in ix.items()}
+        io = torch.empty_like(ig["q"])
+        il = torch.empty(ig["q"].shape[:2], dtype=torch.float32, device=dev)
+        iws = torch.empty(fa.fa_decode_paged_workspace_size(dcfg.num_seqs, dcfg.Hq, dcfg.d, ix["max_pages_per_seq"]),
+                          dtype=torch.uint8, device=dev)
+
+        def int8_decode():
+            fa.fa_decode_paged_int8(ig["q"], ig["kq"], ig["kscale"], ig["vq"], ig["vscale"], ig["page_table"],
+                                    ig["ctx_lens"], out=io, lse=il, workspace=iws)
+
+        for _ in range(max(1, args.warmup // 3)):
+            int8_decode()
+        torch.cuda.synchronize()
+        iev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
+        for i in range(K):
+            iev[i][0].record()
+            int8_decode()
+            iev[i][1].record()
+        torch.cuda.synchronize()
+        i_ms = sum(e[0].elapsed_time(e[1]) for e in iev) / K
+        ctx = ix["ctx_lens"].long()
+        per_tok = dcfg.Hkv * (2 * dcfg.d + 2 * (dcfg.d // 32) * 4)
+        iby = int(ctx.sum()) * per_tok + 2 * dcfg.num_seqs * dcfg.Hq * dcfg.d * 2 + dcfg.num_seqs * dcfg.Hq * 4 + \
+            int(((ctx + 15) // 16).sum()) * 4 + dcfg.num_seqs * 4
+        igbs = iby / (i_ms * 1e-3) / 1e9
+        log(f"int8 decode {i_ms:.4f} ms ({igbs:.1f} GB/s)")
+        d8 = {"value": round(igbs, 1), "unit": "GB/s", "ms": round(i_ms, 5),
+              "roofline": {"bound": "hbm", "achieved": round(igbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                           "frac": round(igbs / PEAK_HBM_GBS, 4), "traffic": None,
+                           "kernel": "decode_split_int8_kernel<128, 4> + decode_merge_kernel<128>",
+                           "algorithmic_bytes_per_launch": iby},
+              "workload": "paged decode 64 seqs Hq32 Hkv8 d128 ctx~U[1024,16384] over an INT8 cache with fp32 "
+                          "scales per 32 channels (288 B per token and K/V head instead of 512)"}
+
     res = {"metric": METRIC, "n_gpus": 1, "steps": K, "warmup": args.warmup, "ms_per_step": round(step_ms, 5),
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
            "data": "synthetic (seeded N(0,1) inputs; random page permutation)"}
@@ -396,6 +439,8 @@ def main():
         res["window_alibi"] = wa
     if cp is not None:
         res["chunked_prefill"] = cp
+    if d8 is not None:
+        res["decode_int8"] = d8
     if bwd is not None:
         res["backward"] = bwd
         if not run_p and not run_d:

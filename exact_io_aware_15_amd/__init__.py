@@ -27,6 +27,7 @@ __all__ = [
     "fa_decode_paged",
     "fa_decode_paged_workspace_size",
     "fa_prefill_paged",
+    "fa_decode_paged_int8",
     "fa_status_string",
     "LIB_PATH",
 ]
@@ -62,6 +63,8 @@ def lib() -> ctypes.CDLL:
     L.fa_bwd_workspace_size.restype = sz
     L.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp, sz, vp]
     L.fa_bwd.restype = i
+    L.fa_decode_paged_int8.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, f, vp, sz, vp]
+    L.fa_decode_paged_int8.restype = i
     L.fa_prefill_paged.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, f, vp]
     L.fa_prefill_paged.restype = i
     L.fa_decode_paged_workspace_size.argtypes = [i, i, i, i, i]
@@ -260,4 +263,39 @@ def fa_prefill_paged(q, kpages, vpages, page_table, ctx_lens, scale=None, out=No
                                 _ptr(lse), S, Hq, Hkv, d, C, page_size, maxp, P, float(scale), _stream(q))
     if st != FA_OK:
         raise FAError(st, "fa_prefill_paged")
+    return out, lse
+
+
+def fa_decode_paged_int8(q, kq, kscale, vq, vscale, page_table, ctx_lens, scale=None, out=None, lse=None,
+                         workspace=None, group=32):
+    """Paged decode over an INT8 cache: kq/vq [P,Hkv,16,d] int8, kscale/vscale [P,Hkv,16,d/group] fp32,
+    other arguments as fa_decode_paged -> (O bf16 [S,Hq,d], L fp32 [S,Hq])."""
+    S, Hq, d = q.shape
+    P, Hkv, page_size, _ = kq.shape
+    maxp = page_table.shape[1]
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on a GPU")
+    _need(q, "q", torch.bfloat16, (S, Hq, d), dev)
+    _need(kq, "kq", torch.int8, (P, Hkv, page_size, d), dev)
+    _need(vq, "vq", torch.int8, (P, Hkv, page_size, d), dev)
+    _need(kscale, "kscale", torch.float32, (P, Hkv, page_size, d // group), dev)
+    _need(vscale, "vscale", torch.float32, (P, Hkv, page_size, d // group), dev)
+    _need(page_table, "page_table", torch.int32, (S, maxp), dev)
+    _need(ctx_lens, "ctx_lens", torch.int32, (S,), dev)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    out = torch.empty((S, Hq, d), dtype=torch.bfloat16, device=dev) if out is None else out
+    lse = torch.empty((S, Hq), dtype=torch.float32, device=dev) if lse is None else lse
+    _need(out, "out", torch.bfloat16, (S, Hq, d), dev)
+    _need(lse, "lse", torch.float32, (S, Hq), dev)
+    need = fa_decode_paged_workspace_size(S, Hq, d, maxp, page_size)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    st = lib().fa_decode_paged_int8(_ptr(q), _ptr(kq), _ptr(kscale), _ptr(vq), _ptr(vscale), _ptr(page_table),
+                                    _ptr(ctx_lens), _ptr(out), _ptr(lse), S, Hq, Hkv, d, page_size, group, maxp, P,
+                                    float(scale), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                    _stream(q))
+    if st != FA_OK:
+        raise FAError(st, "fa_decode_paged_int8")
     return out, lse

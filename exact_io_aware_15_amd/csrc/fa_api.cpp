@@ -164,6 +164,32 @@ int fa_decode_paged(const void* q, const void* kpages, const void* vpages, const
   return finish(fa::launch_decode_paged(a), stream);
 }
 
+int fa_decode_paged_int8(const void* q, const int8_t* kpages, const float* kscale, const int8_t* vpages,
+                         const float* vscale, const int32_t* page_table, const int32_t* ctx_lens, void* o, float* lse,
+                         int num_seqs, int Hq, int Hkv, int d, int page_size, int group, int max_pages_per_seq,
+                         int num_pages, float scale, void* workspace, size_t workspace_bytes, void* stream) {
+  if (num_seqs < 0 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || max_pages_per_seq < 1 || num_pages < 1)
+    return FA_ERR_SHAPE;
+  if ((long long)num_seqs * Hq > 0x7fffffffLL || fa::decode_max_splits(max_pages_per_seq) > 65535)
+    return FA_ERR_SHAPE;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  if (page_size != 16 || group != 32) return FA_ERR_UNSUPPORTED;
+  if (!std::isfinite(scale)) return FA_ERR_SCALE;
+  if (num_seqs == 0) return FA_OK;
+  if (!q || !kpages || !kscale || !vpages || !vscale || !page_table || !ctx_lens || !o || !lse) return FA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(kpages) || !aligned16(vpages) || !aligned16(page_table) || !aligned16(ctx_lens) ||
+      !aligned16(o) || !aligned16(lse) || ((uintptr_t)kscale & 3u) || ((uintptr_t)vscale & 3u))
+    return FA_ERR_ALIGN;
+  const size_t need = fa::decode_workspace_bytes(num_seqs, Hq, d, max_pages_per_seq);
+  if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return FA_ERR_ALIGN;
+  fa::DecodeArgs a{q,  kpages, vpages, page_table, ctx_lens, o, lse, num_seqs, Hq, Hkv, d, page_size,
+                   max_pages_per_seq, scale, workspace, stream};
+  a.kscale = kscale;
+  a.vscale = vscale;
+  return finish(fa::launch_decode_paged(a), stream);
+}
+
 const char* fa_status_string(int status) {
   switch (status) {
     case FA_OK: return "ok";

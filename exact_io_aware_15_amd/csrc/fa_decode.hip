@@ -295,6 +295,253 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
   }
 }
 
+
+// ---------------------------------------------------------------------------
+// INT8 group-scaled KV cache (screna.ai KV-cache quantization block: 8-bit cache
+// with group-wise scales).  K/V pages hold int8 values, one fp32 scale per
+// (page, K/V head, token, 32 consecutive channels); the value is int8 * scale.
+// Same grid, page-id register and ping-pong buffers as decode_split_kernel; lane
+// l holds tokens 2(l/8), 2(l/8)+1 and channels (l%8)*CH .. +CH (one 32-channel
+// group), CH = D/8.  Bytes are read as b + 128 (v_cvt_f32_ubyte after flipping
+// the sign bit) and the offset is removed algebraically: q.k = sum q_c (b_c + 128)
+// - 128 sum q_c, and O += p s (b + 128) - 128 p s per group.  P V runs in fp32, so
+// O is normalised by the exact probability sum.
+template <int CH>
+struct I8Vec;
+template <>
+struct I8Vec<16> {
+  typedef u32x4 T;
+};
+template <>
+struct I8Vec<8> {
+  typedef u32x2 T;
+};
+
+template <int D, int HB>
+__global__ __launch_bounds__(kDecThreads) void decode_split_int8_kernel(
+    const uint16_t* __restrict__ Q, const int8_t* __restrict__ KQ, const float* __restrict__ KS,
+    const int8_t* __restrict__ VQ, const float* __restrict__ VS, const int32_t* __restrict__ table,
+    const int32_t* __restrict__ ctx, float* __restrict__ ws_o, float* __restrict__ ws_l, int Hq, int Hkv,
+    int max_pages, int max_splits, int nhb, float c) {
+  constexpr int CH = D / 8;           // channels per lane
+  constexpr int NG = D / 32;          // scale groups per token
+  constexpr int NW = CH / 4;          // 32-bit words per token per lane
+  constexpr int PP = 2;               // pages consumed per wave iteration
+  typedef typename I8Vec<CH>::T vec_t;
+  __shared__ float sm_m[kDecWaves][HB];
+  __shared__ float sm_l[kDecWaves][HB];
+  __shared__ float sm_acc[kDecWaves][HB][D];
+
+  const int split = blockIdx.y;
+  const int hb = blockIdx.x % nhb;
+  const int g = (blockIdx.x / nhb) % Hkv;
+  const int s = blockIdx.x / (nhb * Hkv);
+  const int G = Hq / Hkv;
+  const int n = ctx[s];
+  const int npages = (n + kPage - 1) / kPage;
+  const int p_begin = split * kDecodePagesPerSplit;
+  if (p_begin >= npages) return;
+  const int p_end = min(npages, p_begin + kDecodePagesPerSplit);
+
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int tg = lane >> 3;
+  const int dg = lane & 7;
+  const int grp = dg * CH / 32;       // the lane's scale group
+
+  // q in fp32 for the lane's channels, and its sum (for the +128 byte offset)
+  float qf[HB][CH], qsum[HB];
+#pragma unroll
+  for (int hh = 0; hh < HB; ++hh) {
+    const int hl = hb * HB + hh;
+    const bool ok = hl < G;
+    const uint16_t* qrow = Q + ((size_t)s * Hq + g * G + (ok ? hl : 0)) * D + dg * CH;
+    float sum = 0.f;
+#pragma unroll
+    for (int e = 0; e < CH / 8; ++e) {
+      const u32x4 x = ldg16(qrow + e * 8);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        qf[hh][e * 8 + 2 * k] = ok ? bf16lo_to_f32(x[k]) : 0.f;
+        qf[hh][e * 8 + 2 * k + 1] = ok ? bf16hi_to_f32(x[k]) : 0.f;
+        sum += qf[hh][e * 8 + 2 * k] + qf[hh][e * 8 + 2 * k + 1];
+      }
+    }
+    qsum[hh] = 128.f * sum;
+  }
+
+  float m_run[HB], l_run[HB], corr[HB], acc[HB][CH];
+#pragma unroll
+  for (int hh = 0; hh < HB; ++hh) {
+    m_run[hh] = -INFINITY;
+    l_run[hh] = 0.f;
+    corr[hh] = 0.f;
+#pragma unroll
+    for (int i = 0; i < CH; ++i) acc[hh][i] = 0.f;
+  }
+
+  constexpr int kIdRegs = (kDecodePagesPerSplit + 63) / 64;
+  const int32_t* trow = table + (size_t)s * max_pages;
+  int lane_pid[kIdRegs];
+#pragma unroll
+  for (int r = 0; r < kIdRegs; ++r) {
+    const int pg = p_begin + 64 * r + (tid & 63);
+    lane_pid[r] = pg < p_end ? trow[pg] : 0;
+  }
+  auto page_id = [&](int idx) {
+    int id = __builtin_amdgcn_readlane(lane_pid[0], idx & 63);
+#pragma unroll
+    for (int r = 1; r < kIdRegs; ++r)
+      if ((idx >> 6) == r) id = __builtin_amdgcn_readlane(lane_pid[r], idx & 63);
+    return id;
+  };
+
+  vec_t ka[PP][2], va[PP][2], kb[PP][2], vb[PP][2];
+  float ksa[PP][2], vsa[PP][2], ksb[PP][2], vsb[PP][2];
+  auto fetch = [&](int p0, vec_t (&kd)[PP][2], vec_t (&vd)[PP][2], float (&ksd)[PP][2], float (&vsd)[PP][2]) {
+#pragma unroll
+    for (int pp = 0; pp < PP; ++pp) {
+      const int p = min(p0 + pp, p_end - 1);
+      const size_t head = (size_t)page_id(p - p_begin) * Hkv + g;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int tok = 2 * tg + j;
+        const size_t off = (head * kPage + tok) * D + dg * CH;
+        kd[pp][j] = *reinterpret_cast<const vec_t*>(KQ + off);
+        vd[pp][j] = *reinterpret_cast<const vec_t*>(VQ + off);
+        ksd[pp][j] = KS[(head * kPage + tok) * NG + grp];
+        vsd[pp][j] = VS[(head * kPage + tok) * NG + grp];
+      }
+    }
+  };
+  auto consume = [&](int p, vec_t (&kc)[PP][2], vec_t (&vc)[PP][2], float (&ksc)[PP][2], float (&vsc)[PP][2]) {
+    float sc[PP][2][HB];
+#pragma unroll
+    for (int pp = 0; pp < PP; ++pp)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const bool valid = (p + pp) * kPage + 2 * tg + j < n && p + pp < p_end;
+        float u[CH];  // byte + 128
+#pragma unroll
+        for (int e = 0; e < NW; ++e) {
+          const uint32_t x = kc[pp][j][e] ^ 0x80808080u;
+#pragma unroll
+          for (int k = 0; k < 4; ++k) u[4 * e + k] = (float)((x >> (8 * k)) & 0xffu);
+        }
+#pragma unroll
+        for (int hh = 0; hh < HB; ++hh) {
+          float part = -qsum[hh];
+#pragma unroll
+          for (int i = 0; i < CH; ++i) part = __builtin_fmaf(qf[hh][i], u[i], part);
+          part = sum8(part * ksc[pp][j]) * c;
+          sc[pp][j][hh] = valid ? part : -INFINITY;
+        }
+      }
+    bool grow = false;
+    float mnew[HB];
+#pragma unroll
+    for (int hh = 0; hh < HB; ++hh) {
+      float pm = fmaxf(sc[0][0][hh], sc[0][1][hh]);
+#pragma unroll
+      for (int pp = 1; pp < PP; ++pp) pm = fmaxf(pm, fmaxf(sc[pp][0][hh], sc[pp][1][hh]));
+      pm = max_stride8(pm);
+      mnew[hh] = fmaxf(m_run[hh], pm);
+      grow |= mnew[hh] > m_run[hh];
+    }
+    if (grow) {
+#pragma unroll
+      for (int hh = 0; hh < HB; ++hh) {
+        const float alpha = exp2_fast(m_run[hh] - mnew[hh]);
+        l_run[hh] *= alpha;
+        corr[hh] *= alpha;
+#pragma unroll
+        for (int i = 0; i < CH; ++i) acc[hh][i] *= alpha;
+        m_run[hh] = mnew[hh];
+      }
+    }
+#pragma unroll
+    for (int pp = 0; pp < PP; ++pp) {
+      float u0[CH], u1[CH];
+#pragma unroll
+      for (int e = 0; e < NW; ++e) {
+        const uint32_t x0 = vc[pp][0][e] ^ 0x80808080u, x1 = vc[pp][1][e] ^ 0x80808080u;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          u0[4 * e + k] = (float)((x0 >> (8 * k)) & 0xffu);
+          u1[4 * e + k] = (float)((x1 >> (8 * k)) & 0xffu);
+        }
+      }
+      const bool v0 = (p + pp) * kPage + 2 * tg < n && p + pp < p_end;
+      const bool v1 = (p + pp) * kPage + 2 * tg + 1 < n && p + pp < p_end;
+#pragma unroll
+      for (int hh = 0; hh < HB; ++hh) {
+        const float p0 = v0 ? exp2_fast(sc[pp][0][hh] - m_run[hh]) : 0.f;
+        const float p1 = v1 ? exp2_fast(sc[pp][1][hh] - m_run[hh]) : 0.f;
+        l_run[hh] += p0 + p1;
+        // invalid tokens (possibly NaN scales) contribute exactly nothing
+        const float ps0 = v0 ? p0 * vsc[pp][0] : 0.f;
+        const float ps1 = v1 ? p1 * vsc[pp][1] : 0.f;
+        corr[hh] += 128.f * (ps0 + ps1);
+#pragma unroll
+        for (int i = 0; i < CH; ++i) acc[hh][i] = __builtin_fmaf(ps1, u1[i], __builtin_fmaf(ps0, u0[i], acc[hh][i]));
+      }
+    }
+  };
+
+  constexpr int kStride = PP * kDecWaves;
+  int p = p_begin + PP * w;
+  if (p < p_end) fetch(p, ka, va, ksa, vsa);
+  while (p < p_end) {
+    fetch(p + kStride < p_end ? p + kStride : p, kb, vb, ksb, vsb);
+    consume(p, ka, va, ksa, vsa);
+    p += kStride;
+    if (p >= p_end) break;
+    fetch(p + kStride < p_end ? p + kStride : p, ka, va, ksa, vsa);
+    consume(p, kb, vb, ksb, vsb);
+    p += kStride;
+  }
+
+  // remove the byte offset, combine the 8 token-pair lanes, then the 4 waves
+#pragma unroll
+  for (int hh = 0; hh < HB; ++hh) {
+    l_run[hh] = sum_stride8(l_run[hh]);
+#pragma unroll
+    for (int i = 0; i < CH; ++i) acc[hh][i] = sum_stride8(acc[hh][i] - corr[hh]);
+  }
+  if (lane < 8) {
+#pragma unroll
+    for (int hh = 0; hh < HB; ++hh) {
+      if (lane == 0) {
+        sm_m[w][hh] = m_run[hh];
+        sm_l[w][hh] = l_run[hh];
+      }
+#pragma unroll
+      for (int i = 0; i < CH; ++i) sm_acc[w][hh][dg * CH + i] = acc[hh][i];
+    }
+  }
+  __syncthreads();
+  for (int i = tid; i < HB * D; i += kDecThreads) {
+    const int hh = i / D, d = i % D;
+    const int hl = hb * HB + hh;
+    if (hl >= G) continue;
+    float M = -INFINITY;
+#pragma unroll
+    for (int ww = 0; ww < kDecWaves; ++ww) M = fmaxf(M, sm_m[ww][hh]);
+    float wsum = 0.f, o = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < kDecWaves; ++ww) {
+      const float mw = sm_m[ww][hh];
+      const float f = (mw == -INFINITY) ? 0.f : exp2_fast(mw - M);
+      wsum += f * sm_l[ww][hh];
+      o += f * sm_acc[ww][hh][d];
+    }
+    const size_t slot = ((size_t)s * Hq + g * G + hl) * max_splits + split;
+    ws_o[slot * D + d] = o / wsum;
+    if (d == 0) ws_l[slot] = M + log2_fast(wsum);
+  }
+}
+
 template <int D>
 __global__ __launch_bounds__(D) void decode_merge_kernel(const float* __restrict__ ws_o,
                                                          const float* __restrict__ ws_l,
@@ -337,6 +584,18 @@ hipError_t launch_split(const DecodeArgs& a, float* ws_o, float* ws_l, int max_s
   return hipGetLastError();
 }
 
+template <int D, int HB>
+hipError_t launch_split_int8(const DecodeArgs& a, float* ws_o, float* ws_l, int max_splits) {
+  const int G = a.Hq / a.Hkv;
+  const int nhb = (G + HB - 1) / HB;
+  const dim3 grid((unsigned)(a.S * a.Hkv * nhb), (unsigned)max_splits);
+  hipLaunchKernelGGL((decode_split_int8_kernel<D, HB>), grid, dim3(kDecThreads), 0, (hipStream_t)a.stream,
+                     (const uint16_t*)a.q, (const int8_t*)a.kpages, a.kscale, (const int8_t*)a.vpages, a.vscale,
+                     a.page_table, a.ctx_lens, ws_o, ws_l, a.Hq, a.Hkv, a.max_pages, max_splits, nhb,
+                     a.scale * kLog2e);
+  return hipGetLastError();
+}
+
 template <int D>
 hipError_t launch_d(const DecodeArgs& a) {
   const int max_splits = decode_max_splits(a.max_pages);
@@ -345,7 +604,11 @@ hipError_t launch_d(const DecodeArgs& a) {
   float* ws_l = (float*)((uint8_t*)a.workspace + ((o_bytes + 255) / 256) * 256);
   const int G = a.Hq / a.Hkv;
   hipError_t e;
-  if (G <= 1) e = launch_split<D, 1>(a, ws_o, ws_l, max_splits);
+  if (a.kscale != nullptr) {
+    if (G <= 1) e = launch_split_int8<D, 1>(a, ws_o, ws_l, max_splits);
+    else if (G <= 2) e = launch_split_int8<D, 2>(a, ws_o, ws_l, max_splits);
+    else e = launch_split_int8<D, 4>(a, ws_o, ws_l, max_splits);
+  } else if (G <= 1) e = launch_split<D, 1>(a, ws_o, ws_l, max_splits);
   else if (G <= 2) e = launch_split<D, 2>(a, ws_o, ws_l, max_splits);
   else e = launch_split<D, 4>(a, ws_o, ws_l, max_splits);
   if (e != hipSuccess) return e;

@@ -39,6 +39,10 @@ struct DecodeArgs {
   float scale;
   void* workspace;
   void* stream;
+  // INT8 cache (fa_decode_paged_int8): kpages/vpages hold int8, with one fp32 scale
+  // per (page, head, token, 32 channels) in kscale/vscale; nullptr = bf16 cache
+  const float* kscale = nullptr;
+  const float* vscale = nullptr;
 };
 
 // Pages handled by one split of the paged decode.  The workspace size depends on it.

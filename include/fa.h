@@ -210,6 +210,30 @@ int fa_decode_paged(const void* q, const void* kpages, const void* vpages,
                     void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * fa_decode_paged_int8 -- fa_decode_paged over an INT8 KV cache with group-wise
+ * scales (half the cache bytes of bf16, plus the scales).
+ *
+ * Pages: screna.ai KV-cache quantization block (an 8-bit cache halves the KV
+ * memory; group-wise scales keep the accuracy of per-tensor ones or better) and
+ * "Phase 08", Lab 03 step 4 (paged attention).  The cached value of channel c of
+ * token t is kpages[pg][h][t][c] * kscale[pg][h][t][c / group] (V alike).
+ *
+ *   kpages, vpages  [num_pages, Hkv, page_size, d] int8, 16-byte aligned
+ *   kscale, vscale  [num_pages, Hkv, page_size, d / group] fp32, 4-byte aligned
+ *   group           32 (channels per scale); other values FA_ERR_UNSUPPORTED
+ *   everything else (q, o, lse, page_table, ctx_lens, workspace and its size from
+ *   fa_decode_paged_workspace_size, status codes) as fa_decode_paged.  Slots at or
+ *   beyond ctx_lens[s] never affect the result, whatever values or scales they hold.
+ */
+int fa_decode_paged_int8(const void* q, const int8_t* kpages, const float* kscale,
+                         const int8_t* vpages, const float* vscale,
+                         const int32_t* page_table, const int32_t* ctx_lens,
+                         void* o, float* lse, int num_seqs, int Hq, int Hkv, int d,
+                         int page_size, int group, int max_pages_per_seq,
+                         int num_pages, float scale, void* workspace,
+                         size_t workspace_bytes, void* stream);
+
+/*
  * fa_status_string -- static text for a status code.  For FA_ERR_HIP it is the
  * text of the last HIP error seen by the calling thread.
  */

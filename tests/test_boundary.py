@@ -32,7 +32,7 @@ def L():
 
 def test_every_declared_symbol_is_exported(L):
     names = declared_functions()
-    assert set(names) >= {"fa_fwd", "fa_fwd_f32", "fa_fwd_ex", "fa_prefill_paged", "fa_bwd", "fa_bwd_workspace_size", "fa_decode_paged",
+    assert set(names) >= {"fa_fwd", "fa_fwd_f32", "fa_fwd_ex", "fa_prefill_paged", "fa_decode_paged_int8", "fa_bwd", "fa_bwd_workspace_size", "fa_decode_paged",
                           "fa_decode_paged_workspace_size", "fa_status_string"}
     for n in names:
         assert hasattr(L, n), n
@@ -172,3 +172,20 @@ def test_prefill_paged_validation(L):
     assert pp(L, o=MIS) == ALIGN
     assert pp(L, q=Z, kp=Z, vp=Z, pt=Z, cl=Z, o=Z, lse=Z, C=0) == OK
     assert pp(L, q=Z, kp=Z, vp=Z, pt=Z, cl=Z, o=Z, lse=Z, S=0) == OK
+
+
+def d8(L, q=P, kq=P, ks=P, vq=P, vs=P, pt=P, cl=P, o=P, lse=P, S=2, Hq=8, Hkv=2, d=128, ps=16, group=32, maxp=4,
+       npages=9, scale=0.1, ws=P, wsb=1 << 30):
+    return L.fa_decode_paged_int8(q, kq, ks, vq, vs, pt, cl, o, lse, S, Hq, Hkv, d, ps, group, maxp, npages, scale, ws,
+                                  wsb, Z)
+
+
+def test_decode_int8_validation(L):
+    assert d8(L, ks=Z) == NULL
+    assert d8(L, group=64) == UNSUP
+    assert d8(L, d=80) == UNSUP
+    assert d8(L, Hq=6, Hkv=4) == SHAPE
+    assert d8(L, vs=ctypes.c_void_p(0x10002)) == ALIGN
+    assert d8(L, kq=MIS) == ALIGN
+    assert d8(L, ws=Z) == WORKSPACE
+    assert d8(L, q=Z, kq=Z, ks=Z, vq=Z, vs=Z, pt=Z, cl=Z, o=Z, lse=Z, ws=Z, S=0) == OK
