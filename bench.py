@@ -203,6 +203,7 @@ def main():
     run_p = args.only in (None, "prefill")
     run_d = args.only in (None, "decode")
     run_b = args.only == "backward" or (args.only is None and not args.no_bwd)
+    run_x = args.only is None  # the measurements beside the step (window, chunked, int8)
 
     log("generating inputs")
     px = make_inputs(pcfg) if run_p else None
@@ -255,12 +256,13 @@ def main():
     log(f"prefill {p_ms:.4f} ms, decode {d_ms:.4f} ms, step {step_ms:.4f} ms (wall {wall * 1e3 / K:.4f} ms)")
 
     bwd = None
+    if run_b or run_x:
+        bx = px if px is not None else make_inputs(pcfg)
+        bq, bk, bv = (bx[n].to(dev) for n in "qkv")
     if run_b:
         # the backward (not part of the step): gradients of the same causal prefill for a
         # seeded upstream gradient, with O and L from the forward computed beforehand
         from exact_io_aware_15_amd.workloads import make_grad_output
-        bx = px if px is not None else make_inputs(pcfg)
-        bq, bk, bv = (bx[n].to(dev) for n in "qkv")
         bdo_cpu = make_grad_output(pcfg.B, pcfg.Hq, pcfg.N, pcfg.d, seed=pcfg.seed)
         bdo = bdo_cpu.to(dev)
         bo, bl = fa.fa_fwd(bq, bk, bv, causal=pcfg.causal, scale=pcfg.scale)
@@ -294,7 +296,7 @@ def main():
                            "forward's (five N x N x d products), causal half"}
 
     wa = None
-    if run_b and not args.no_window:
+    if run_x and not args.no_window:
         # sliding window (W = 4096) + ALiBi on the same causal prefill (not part of the step);
         # FLOPs count only the visible (query, key) pairs: sum_i min(i + 1, W)
         from exact_io_aware_15_amd.workloads import make_alibi_slopes
@@ -329,7 +331,7 @@ def main():
                           "slopes 2^(-8(h+1)/32); FLOPs over visible pairs only"}
 
     cp = None
-    if run_b and not args.no_chunked:
+    if run_x and not args.no_chunked:
         # chunked prefill over a paged cache (not part of the step): 16 sequences, 512-token
         # chunks, contexts U[512, 16384], Hq32 Hkv8 d128; FLOPs over the visible pairs
         from exact_io_aware_15_amd.workloads import make_prefill_paged
@@ -365,7 +367,7 @@ def main():
                           f"U[512,16384] (total {int(ctxs.sum())}), Hq32 Hkv8 d128; FLOPs over visible pairs"}
 
     d8 = None
-    if run_b and not args.no_int8:
+    if run_x and not args.no_int8:
         # INT8 group-scaled paged decode on the decode workload's shapes and seed (not part
         # of the step); algorithmic bytes: int8 K/V and their fp32 scales of every valid
         # token, plus q, O, L, the used page-table entries and ctx_lens

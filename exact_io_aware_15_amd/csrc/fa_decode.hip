@@ -304,8 +304,10 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
 // l holds tokens 2(l/8), 2(l/8)+1 and channels (l%8)*CH .. +CH (one 32-channel
 // group), CH = D/8.  Bytes are read as b + 128 (v_cvt_f32_ubyte after flipping
 // the sign bit) and the offset is removed algebraically: q.k = sum q_c (b_c + 128)
-// - 128 sum q_c, and O += p s (b + 128) - 128 p s per group.  P V runs in fp32, so
-// O is normalised by the exact probability sum.
+// - 128 sum q_c, and O += p s (b + 128) - 128 p s per group.  Both products run as
+// bf16 pair dot products (the offset bytes 1 .. 255 are exact in bf16); p s enters P V
+// rounded to bf16 and O is normalised by the sum of the rounded probabilities, L by
+// the fp32 sum.
 template <int CH>
 struct I8Vec;
 template <>
@@ -330,6 +332,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_int8_kernel(
   typedef typename I8Vec<CH>::T vec_t;
   __shared__ float sm_m[kDecWaves][HB];
   __shared__ float sm_l[kDecWaves][HB];
+  __shared__ float sm_lr[kDecWaves][HB];
   __shared__ float sm_acc[kDecWaves][HB][D];
 
   const int split = blockIdx.y;
@@ -350,8 +353,10 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_int8_kernel(
   const int dg = lane & 7;
   const int grp = dg * CH / 32;       // the lane's scale group
 
-  // q in fp32 for the lane's channels, and its sum (for the +128 byte offset)
-  float qf[HB][CH], qsum[HB];
+  // q as bf16 channel pairs (dot2 operands) for the lane's channels, and 128 * sum q
+  // (the byte offset correction)
+  uint32_t qp[HB][CH / 2];
+  float qsum[HB];
 #pragma unroll
   for (int hh = 0; hh < HB; ++hh) {
     const int hl = hb * HB + hh;
@@ -363,19 +368,21 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_int8_kernel(
       const u32x4 x = ldg16(qrow + e * 8);
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        qf[hh][e * 8 + 2 * k] = ok ? bf16lo_to_f32(x[k]) : 0.f;
-        qf[hh][e * 8 + 2 * k + 1] = ok ? bf16hi_to_f32(x[k]) : 0.f;
-        sum += qf[hh][e * 8 + 2 * k] + qf[hh][e * 8 + 2 * k + 1];
+        qp[hh][e * 4 + k] = ok ? x[k] : 0u;
+        sum += ok ? bf16lo_to_f32(x[k]) + bf16hi_to_f32(x[k]) : 0.f;
       }
     }
     qsum[hh] = 128.f * sum;
   }
 
-  float m_run[HB], l_run[HB], corr[HB], acc[HB][CH];
+  // running max, sums of the fp32 probabilities (L) and of their bf16 roundings (O),
+  // the offset correction and the unnormalised output accumulator
+  float m_run[HB], l_run[HB], l_rnd[HB], corr[HB], acc[HB][CH];
 #pragma unroll
   for (int hh = 0; hh < HB; ++hh) {
     m_run[hh] = -INFINITY;
     l_run[hh] = 0.f;
+    l_rnd[hh] = 0.f;
     corr[hh] = 0.f;
 #pragma unroll
     for (int i = 0; i < CH; ++i) acc[hh][i] = 0.f;
@@ -422,18 +429,20 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_int8_kernel(
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const bool valid = (p + pp) * kPage + 2 * tg + j < n && p + pp < p_end;
-        float u[CH];  // byte + 128
+        // byte + 128 (1 .. 255, exact in bf16) as bf16 channel pairs
+        uint32_t up[CH / 2];
 #pragma unroll
         for (int e = 0; e < NW; ++e) {
           const uint32_t x = kc[pp][j][e] ^ 0x80808080u;
-#pragma unroll
-          for (int k = 0; k < 4; ++k) u[4 * e + k] = (float)((x >> (8 * k)) & 0xffu);
+          up[2 * e] = pack_bf16x2((float)(x & 0xffu), (float)((x >> 8) & 0xffu));
+          up[2 * e + 1] = pack_bf16x2((float)((x >> 16) & 0xffu), (float)(x >> 24));
         }
 #pragma unroll
         for (int hh = 0; hh < HB; ++hh) {
           float part = -qsum[hh];
 #pragma unroll
-          for (int i = 0; i < CH; ++i) part = __builtin_fmaf(qf[hh][i], u[i], part);
+          for (int i = 0; i < CH / 2; ++i)
+            part = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(qp[hh][i]), as_bf16x2(up[i]), part, false);
           part = sum8(part * ksc[pp][j]) * c;
           sc[pp][j][hh] = valid ? part : -INFINITY;
         }
@@ -454,23 +463,24 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_int8_kernel(
       for (int hh = 0; hh < HB; ++hh) {
         const float alpha = exp2_fast(m_run[hh] - mnew[hh]);
         l_run[hh] *= alpha;
+        l_rnd[hh] *= alpha;
         corr[hh] *= alpha;
 #pragma unroll
         for (int i = 0; i < CH; ++i) acc[hh][i] *= alpha;
         m_run[hh] = mnew[hh];
       }
     }
+    const bf16x2 ones = as_bf16x2(0x3f803f80u);
 #pragma unroll
     for (int pp = 0; pp < PP; ++pp) {
-      float u0[CH], u1[CH];
+      // channel c of the two tokens as one bf16 pair (byte + 128 of token 0, token 1)
+      uint32_t vp[CH];
 #pragma unroll
       for (int e = 0; e < NW; ++e) {
         const uint32_t x0 = vc[pp][0][e] ^ 0x80808080u, x1 = vc[pp][1][e] ^ 0x80808080u;
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          u0[4 * e + k] = (float)((x0 >> (8 * k)) & 0xffu);
-          u1[4 * e + k] = (float)((x1 >> (8 * k)) & 0xffu);
-        }
+        for (int k = 0; k < 4; ++k)
+          vp[4 * e + k] = pack_bf16x2((float)((x0 >> (8 * k)) & 0xffu), (float)((x1 >> (8 * k)) & 0xffu));
       }
       const bool v0 = (p + pp) * kPage + 2 * tg < n && p + pp < p_end;
       const bool v1 = (p + pp) * kPage + 2 * tg + 1 < n && p + pp < p_end;
@@ -479,12 +489,17 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_int8_kernel(
         const float p0 = v0 ? exp2_fast(sc[pp][0][hh] - m_run[hh]) : 0.f;
         const float p1 = v1 ? exp2_fast(sc[pp][1][hh] - m_run[hh]) : 0.f;
         l_run[hh] += p0 + p1;
-        // invalid tokens (possibly NaN scales) contribute exactly nothing
-        const float ps0 = v0 ? p0 * vsc[pp][0] : 0.f;
-        const float ps1 = v1 ? p1 * vsc[pp][1] : 0.f;
-        corr[hh] += 128.f * (ps0 + ps1);
+        // the probabilities enter P V as bf16 pairs; O is later divided by the sum of
+        // those rounded values (L uses the fp32 sum).  Invalid tokens (possibly NaN
+        // scales) contribute exactly nothing.
+        const uint32_t pr = pack_bf16x2(p0, p1);
+        l_rnd[hh] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(pr), ones, l_rnd[hh], false);
+        const float s0 = v0 ? vsc[pp][0] : 0.f, s1 = v1 ? vsc[pp][1] : 0.f;
+        const uint32_t ps = pack_bf16x2(bf16lo_to_f32(pr) * s0, bf16hi_to_f32(pr) * s1);
+        corr[hh] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(ps), as_bf16x2(0x43004300u), corr[hh], false);
 #pragma unroll
-        for (int i = 0; i < CH; ++i) acc[hh][i] = __builtin_fmaf(ps1, u1[i], __builtin_fmaf(ps0, u0[i], acc[hh][i]));
+        for (int i = 0; i < CH; ++i)
+          acc[hh][i] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(ps), as_bf16x2(vp[i]), acc[hh][i], false);
       }
     }
   };
@@ -506,6 +521,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_int8_kernel(
 #pragma unroll
   for (int hh = 0; hh < HB; ++hh) {
     l_run[hh] = sum_stride8(l_run[hh]);
+    l_rnd[hh] = sum_stride8(l_rnd[hh]);
 #pragma unroll
     for (int i = 0; i < CH; ++i) acc[hh][i] = sum_stride8(acc[hh][i] - corr[hh]);
   }
@@ -515,6 +531,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_int8_kernel(
       if (lane == 0) {
         sm_m[w][hh] = m_run[hh];
         sm_l[w][hh] = l_run[hh];
+        sm_lr[w][hh] = l_rnd[hh];
       }
 #pragma unroll
       for (int i = 0; i < CH; ++i) sm_acc[w][hh][dg * CH + i] = acc[hh][i];
@@ -528,16 +545,17 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_int8_kernel(
     float M = -INFINITY;
 #pragma unroll
     for (int ww = 0; ww < kDecWaves; ++ww) M = fmaxf(M, sm_m[ww][hh]);
-    float wsum = 0.f, o = 0.f;
+    float wsum = 0.f, rsum = 0.f, o = 0.f;
 #pragma unroll
     for (int ww = 0; ww < kDecWaves; ++ww) {
       const float mw = sm_m[ww][hh];
       const float f = (mw == -INFINITY) ? 0.f : exp2_fast(mw - M);
       wsum += f * sm_l[ww][hh];
+      rsum += f * sm_lr[ww][hh];
       o += f * sm_acc[ww][hh][d];
     }
     const size_t slot = ((size_t)s * Hq + g * G + hl) * max_splits + split;
-    ws_o[slot * D + d] = o / wsum;
+    ws_o[slot * D + d] = o / rsum;
     if (d == 0) ws_l[slot] = M + log2_fast(wsum);
   }
 }
