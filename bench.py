@@ -50,6 +50,9 @@ KERNEL_SOURCES = {
     "prefill": ["fa_device.h", "fa_launch.h", "fa_prefill_bf16.hip"],
     "decode": ["fa_device.h", "fa_launch.h", "fa_decode.hip"],
     "backward": ["fa_device.h", "fa_launch.h", "fa_backward.hip"],
+    "window": ["fa_device.h", "fa_launch.h", "fa_prefill_bf16.hip"],
+    "chunked": ["fa_device.h", "fa_launch.h", "fa_prefill_bf16.hip"],
+    "int8": ["fa_device.h", "fa_launch.h", "fa_decode.hip"],
 }
 
 
@@ -161,7 +164,7 @@ def main():
                     help="oracle backward baseline on the first n query heads of batch 0")
     ap.add_argument("--cpu-decode-seqs", type=int, default=64,
                     help="oracle baseline on the first n sequences of the decode (64 = the whole workload)")
-    ap.add_argument("--only", choices=["prefill", "decode", "backward"], default=None,
+    ap.add_argument("--only", choices=["prefill", "decode", "backward", "window", "chunked", "int8"], default=None,
                     help="time one part only (for profiling runs)")
     ap.add_argument("--no-int8", action="store_true",
                     help="skip the INT8-cache decode measurement (reported beside the step)")
@@ -203,7 +206,10 @@ def main():
     run_p = args.only in (None, "prefill")
     run_d = args.only in (None, "decode")
     run_b = args.only == "backward" or (args.only is None and not args.no_bwd)
-    run_x = args.only is None  # the measurements beside the step (window, chunked, int8)
+    # the measurements beside the step
+    run_w = args.only == "window" or (args.only is None and not args.no_window)
+    run_c = args.only == "chunked" or (args.only is None and not args.no_chunked)
+    run_i = args.only == "int8" or (args.only is None and not args.no_int8)
 
     log("generating inputs")
     px = make_inputs(pcfg) if run_p else None
@@ -256,7 +262,7 @@ def main():
     log(f"prefill {p_ms:.4f} ms, decode {d_ms:.4f} ms, step {step_ms:.4f} ms (wall {wall * 1e3 / K:.4f} ms)")
 
     bwd = None
-    if run_b or run_x:
+    if run_b or run_w:
         bx = px if px is not None else make_inputs(pcfg)
         bq, bk, bv = (bx[n].to(dev) for n in "qkv")
     if run_b:
@@ -296,7 +302,7 @@ def main():
                            "forward's (five N x N x d products), causal half"}
 
     wa = None
-    if run_x and not args.no_window:
+    if run_w:
         # sliding window (W = 4096) + ALiBi on the same causal prefill (not part of the step);
         # FLOPs count only the visible (query, key) pairs: sum_i min(i + 1, W)
         from exact_io_aware_15_amd.workloads import make_alibi_slopes
@@ -324,14 +330,14 @@ def main():
         log(f"window+alibi {w_ms:.4f} ms ({wtf:.1f} TFLOP/s)")
         wa = {"value": round(wtf, 2), "unit": "TFLOP/s", "ms": round(w_ms, 5),
               "roofline": {"bound": "mfma", "achieved": round(wtf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                           "frac": round(wtf / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                           "frac": round(wtf / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic("window"),
                            "kernel": "fwd_bf16_kernel<128, causal, window/ALiBi>",
                            "algorithmic_flops_per_launch": wfl},
               "workload": f"causal bf16 prefill B1 Hq32 N8192 d128 with a {W}-key sliding window and ALiBi "
                           "slopes 2^(-8(h+1)/32); FLOPs over visible pairs only"}
 
     cp = None
-    if run_x and not args.no_chunked:
+    if run_c:
         # chunked prefill over a paged cache (not part of the step): 16 sequences, 512-token
         # chunks, contexts U[512, 16384], Hq32 Hkv8 d128; FLOPs over the visible pairs
         from exact_io_aware_15_amd.workloads import make_prefill_paged
@@ -361,13 +367,13 @@ def main():
         log(f"chunked prefill {c_ms:.4f} ms ({ctf:.1f} TFLOP/s)")
         cp = {"value": round(ctf, 2), "unit": "TFLOP/s", "ms": round(c_ms, 5),
               "roofline": {"bound": "mfma", "achieved": round(ctf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                           "frac": round(ctf / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                           "frac": round(ctf / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic("chunked"),
                            "kernel": "fwd_bf16_kernel<128, causal, paged>", "algorithmic_flops_per_launch": cfl},
               "workload": "chunked prefill over 16-token pages: 16 sequences x 512-token chunks, contexts "
                           f"U[512,16384] (total {int(ctxs.sum())}), Hq32 Hkv8 d128; FLOPs over visible pairs"}
 
     d8 = None
-    if run_x and not args.no_int8:
+    if run_i:
         # INT8 group-scaled paged decode on the decode workload's shapes and seed (not part
         # of the step); algorithmic bytes: int8 K/V and their fp32 scales of every valid
         # token, plus q, O, L, the used page-table entries and ctx_lens
@@ -401,7 +407,7 @@ def main():
         log(f"int8 decode {i_ms:.4f} ms ({igbs:.1f} GB/s)")
         d8 = {"value": round(igbs, 1), "unit": "GB/s", "ms": round(i_ms, 5),
               "roofline": {"bound": "hbm", "achieved": round(igbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                           "frac": round(igbs / PEAK_HBM_GBS, 4), "traffic": None,
+                           "frac": round(igbs / PEAK_HBM_GBS, 4), "traffic": measured_traffic("int8"),
                            "kernel": "decode_split_int8_kernel<128, 4> + decode_merge_kernel<128>",
                            "algorithmic_bytes_per_launch": iby},
               "workload": "paged decode 64 seqs Hq32 Hkv8 d128 ctx~U[1024,16384] over an INT8 cache with fp32 "
@@ -445,8 +451,9 @@ def main():
         res["decode_int8"] = d8
     if bwd is not None:
         res["backward"] = bwd
-        if not run_p and not run_d:
-            res.update({"value": bwd["value"], "unit": "TFLOP/s", "roofline": bwd["roofline"]})
+    if "value" not in res:  # one of the measurements beside the step was run alone
+        one = next(x for x in (bwd, wa, cp, d8) if x is not None)
+        res.update({"value": one["value"], "unit": one["unit"], "roofline": one["roofline"]})
     res["config"] = cfg_desc
     if not args.no_cpu_baseline:
         log("timing the fp64 CPU oracle on a bounded sample")
