@@ -188,8 +188,13 @@ __device__ __forceinline__ void softmax_pack(const f32x16 (&s)[2], WaveState<D>&
 // logits x = s*c - slope2*|i - j| (slope2 = ALiBi slope * log2 e; base = i - j0 - 4hi,
 // so i - j = base - koff), masked on both sides (lo <= koff <= lim), then fed to
 // the same online softmax with unit scale.
+// kb and vb are restrict: the copies in flight during a tile only write the other
+// LDS slot (every read of a slot follows the wait and barrier that end the slot's
+// copy), which lets the compiler drop the wait for all outstanding HBM -> LDS
+// copies that it would otherwise put before the first transposing V read.
 template <int D, bool MASK, bool EXT>
-__device__ __forceinline__ void process_tile(WaveState<D>& st, const uint8_t* kb, const uint8_t* vb,
+__device__ __forceinline__ void process_tile(WaveState<D>& st, const uint8_t* __restrict__ kb,
+                                             const uint8_t* __restrict__ vb,
                                              const int (&koff)[D / 16], const int (&voff)[D / 32], int lim,
                                              int l32, float c, int lo = 0, float base = 0.f, float slope2 = 0.f) {
   using LY = Lay<D>;
@@ -341,12 +346,34 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void fwd_bf16_kernel(
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kStages * LY::TBYTES];
 
   const int nqb = (N + kBR - 1) / kBR;
-  const int BH = B * Hq;
-  // causal: heaviest query blocks are dispatched first
-  const int qb = CAUSAL ? (nqb - 1 - (int)(blockIdx.x / BH)) : (int)(blockIdx.x / BH);
-  const int bh = blockIdx.x % BH;
-  const int b = bh / Hq, h = bh % Hq;
-  const int g = h / (Hq / Hkv);
+  const int G = Hq / Hkv;
+  // Work order: (query block, batch, K/V head, query head in group), causal blocks
+  // heaviest first; paged: (sequence, K/V head, query block, query head in group).
+  // The workgroups that read the same K/V (the G query heads of a group, and when
+  // paged also the chunk's query blocks) are consecutive in that order.  Workgroups
+  // are dealt to the 8 XCDs round-robin by linear index, so runs of S consecutive
+  // items are handed to one XCD (slot s of XCD x takes item (x + 8 (s / S)) S + s % S)
+  // and their K/V tiles are fetched from HBM once into that XCD's L2.  A ragged tail
+  // of fewer than 8 S items keeps the plain order.
+  const int S = PAGED ? G * nqb : G;
+  int item = (int)blockIdx.x;
+  if (item < (int)(gridDim.x / (8 * S)) * 8 * S) item = ((item & 7) + 8 * ((item >> 3) / S)) * S + (item >> 3) % S;
+  int qb, b, h;
+  if constexpr (PAGED) {
+    const int per_seq = Hkv * nqb * G;
+    b = item / per_seq;
+    const int r = item % per_seq;
+    const int gg = r / (nqb * G), r2 = r % (nqb * G);
+    qb = nqb - 1 - r2 / G;
+    h = gg * G + r2 % G;
+  } else {
+    const int BH = B * Hq;
+    qb = CAUSAL ? (nqb - 1 - item / BH) : item / BH;
+    const int bh = item % BH;
+    b = bh / Hq;
+    h = bh % Hq;
+  }
+  const int g = h / G;
 
   const int tid = threadIdx.x;
   const int w = tid >> 6;
