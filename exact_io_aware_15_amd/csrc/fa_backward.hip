@@ -26,6 +26,8 @@
 // heads of its group; when there are too few (key block, K/V head) pairs to fill
 // the GPU (multi-query), the group's heads are split into chunks whose fp32 partial
 // sums a last kernel adds up.
+#include <type_traits>
+
 #include "fa_device.h"
 #include "fa_launch.h"
 
@@ -240,9 +242,10 @@ __global__ __launch_bounds__(kDqWaves * 64, 1) void bwd_dq_kernel(
         copy_tile<D, kDqWaves>(smem + (3 - u) * L::TBYTES, vbase, head_bytes, cp, j0 + kTile, w);
       }
       const bool skip = CAUSAL && (j0 > rw0 + kWaveRows - 1);
-      if (!skip) {
-        const uint8_t* kb = smem + u * L::TBYTES;
-        const uint8_t* vb = smem + (2 + u) * L::TBYTES;
+      // restrict LDS tile pointers: the copy in flight writes only the other buffer,
+      // so the reads need not wait for it (the compiler otherwise waits for all
+      // outstanding copies before the first LDS read that might alias them)
+      auto tile = [&](const uint8_t* __restrict__ kb, const uint8_t* __restrict__ vb) {
         // S^T = K Q^T and dP^T = V dO^T; lane holds keys a*32 + 8(r/4) + 4hi + r%4 of its row
         f32x16 s[2], dp[2];
 #pragma unroll
@@ -303,7 +306,8 @@ __global__ __launch_bounds__(kDqWaves * 64, 1) void bwd_dq_kernel(
                                                                 0, 0, 0);
             }
         sched_reads_ahead<4 * DB, 2, 1, kAhead>();
-      }
+      };
+      if (!skip) tile(smem + u * L::TBYTES, smem + (2 + u) * L::TBYTES);
       __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): tile t+1 has landed
       __syncthreads();
     }
@@ -339,16 +343,93 @@ struct ItemSrc {
 // Start the HBM -> LDS copies of one item into buffer buf: its Q and dO tiles
 // (all waves) and the 64 rows' L (wave 0) and D (wave 1).
 template <int D>
-__device__ __forceinline__ void issue_item(const ItemSrc& s, uint8_t* smem, float (*rowv)[2][kTile], int item,
-                                           int buf) {
+__device__ __forceinline__ void issue_item(const ItemSrc& s, uint8_t* qdst, uint8_t* gdst, float (*rowv)[2][kTile],
+                                           int item, int buf) {
   using L = BLay<D>;
   const int h = s.h_begin + item / s.per_head;
   const int r0 = (s.t_first + item % s.per_head) * kTile;
   const size_t qo = (size_t)(s.b * s.Hq + h) * s.N;
-  copy_tile<D>(smem + buf * L::TBYTES, s.Q + qo * D, s.head_bytes, s.cp, r0, s.w);
-  copy_tile<D>(smem + (2 + buf) * L::TBYTES, s.dO + qo * D, s.head_bytes, s.cp, r0, s.w);
+  copy_tile<D>(qdst, s.Q + qo * D, s.head_bytes, s.cp, r0, s.w);
+  copy_tile<D>(gdst, s.dO + qo * D, s.head_bytes, s.cp, r0, s.w);
   if (s.w == 0) copy_rowvals(rowv[buf][0], s.Lse + qo, s.N, r0, s.lane);
   if (s.w == 1) copy_rowvals(rowv[buf][1], s.Dlt + qo, s.N, r0, s.lane);
+}
+
+// One streamed item (a query head's 64-row Q/dO tile with its rows' L and D) of the
+// dK/dV kernel for this wave's 32 keys: S = Q K^T, dP = dO V^T, P, dS, then
+// dV += P^T dO and dK += dS^T Q.  RP / RF are the LDS pointer types (restrict or
+// plain, chosen by the kernel).
+template <int D, bool CAUSAL, typename RP, typename RF>
+__device__ __forceinline__ void dkdv_tile(RP qb_, RP gb_, RF lrow, RF drow, int r0, int kw0, int key, int N, int hi,
+                                          float cs, const int (&roff)[D / 16], const int (&tlo)[D / 32],
+                                          const int (&thi)[D / 32], const bf16x8 (&kf)[D / 16],
+                                          const bf16x8 (&vf)[D / 16], f32x16 (&dka)[D / 32], f32x16 (&dva)[D / 32]) {
+  using L = BLay<D>;
+  constexpr int KK = D / 16, DB = D / 32;
+  constexpr int kAhead = ahead_for<D>();
+  const bool need_mask = (CAUSAL && r0 < kw0 + kWaveRows - 1) || (r0 + kTile > N);
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb) {
+    // S = Q K^T and dP = dO V^T for rows rb*32 + 8(r/4) + 4hi + r%4 of the tile
+    f32x16 s, dp;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      s[r] = 0.f;
+      dp[r] = 0.f;
+    }
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      const bf16x8 qa = *reinterpret_cast<const bf16x8*>(qb_ + rb * 32 * L::ROWB + roff[kk]);
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[kk], s, 0, 0, 0);
+    }
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      const bf16x8 ga = *reinterpret_cast<const bf16x8*>(gb_ + rb * 32 * L::ROWB + roff[kk]);
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga, vf[kk], dp, 0, 0, 0);
+    }
+    sched_reads_ahead<2 * KK, 1, 2, kAhead>();
+    // P and dS for the lane's key and 16 rows; row values from LDS, 4 rows per read
+    bf16x8 pb[2], dsb[2];
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      u32x4 pk, dk;
+#pragma unroll
+      for (int q4 = 0; q4 < 2; ++q4) {
+        const int rr = rb * 32 + 16 * s2 + 8 * q4 + 4 * hi;  // first of 4 consecutive rows
+        const f32x4 lv = *reinterpret_cast<const f32x4*>(lrow + rr);
+        const f32x4 dv = *reinterpret_cast<const f32x4*>(drow + rr);
+        float pv[4], dsv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = 8 * s2 + 4 * q4 + i;  // accumulator index of row rr + i
+          float p = exp2_fast(__builtin_fmaf(s[r], cs, -lv[i] * kLog2e));
+          const int row = r0 + rr + i;
+          if (need_mask && ((CAUSAL && key > row) || row >= N)) p = 0.f;
+          pv[i] = p;
+          dsv[i] = p * (dp[r] - dv[i]);
+        }
+        pk[2 * q4] = pack_bf16x2(pv[0], pv[1]);
+        pk[2 * q4 + 1] = pack_bf16x2(pv[2], pv[3]);
+        dk[2 * q4] = pack_bf16x2(dsv[0], dsv[1]);
+        dk[2 * q4 + 1] = pack_bf16x2(dsv[2], dsv[3]);
+      }
+      pb[s2] = __builtin_bit_cast(bf16x8, pk);
+      dsb[s2] = __builtin_bit_cast(bf16x8, dk);
+    }
+    // dV += P^T dO, dK += dS^T Q over the 32 rows (two 16-row steps)
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const int r0g = (rb * 32 + 16 * s2) * L::ROWB;
+        dva[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pb[s2], tr_frag(gb_ + r0g, tlo[db], thi[db]), dva[db],
+                                                          0, 0, 0);
+        dka[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dsb[s2], tr_frag(qb_ + r0g, tlo[db], thi[db]), dka[db],
+                                                          0, 0, 0);
+      }
+    sched_reads_ahead<4 * DB, 2, 3, kAhead>();
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -364,7 +445,19 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(
   using L = BLay<D>;
   constexpr int KK = D / 16, DB = D / 32;
   constexpr int kAhead = ahead_for<D>();
-  __shared__ __attribute__((aligned(16))) uint8_t smem[4 * L::TBYTES];  // Q[2], dO[2]
+  // Q and dO tiles, two buffers each.  At d = 128 the four are separate arrays, so the
+  // compiler can tell a tile's reads from the next item's copies into the other
+  // buffers and does not wait for those copies mid-tile; at d = 64 one array (with
+  // that wait) measured faster.
+  constexpr bool kSplitBufs = D == 128;
+  __shared__ __attribute__((aligned(16))) uint8_t sm0[kSplitBufs ? L::TBYTES : 4 * L::TBYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t sm1[kSplitBufs ? L::TBYTES : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t sm2[kSplitBufs ? L::TBYTES : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t sm3[kSplitBufs ? L::TBYTES : 16];
+  uint8_t* const smq0 = sm0;
+  uint8_t* const smq1 = kSplitBufs ? sm1 : sm0 + L::TBYTES;
+  uint8_t* const smg0 = kSplitBufs ? sm2 : sm0 + 2 * L::TBYTES;
+  uint8_t* const smg1 = kSplitBufs ? sm3 : sm0 + 3 * L::TBYTES;
   __shared__ __attribute__((aligned(16))) float rowv[2][2][kTile];      // [buffer][L, D][row]
 
   const int G = Hq / Hkv;
@@ -420,7 +513,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(
   const int total = nh * per_head;
 
   const ItemSrc src{Q, dO, Lse, Dlt, b, Hq, N, h_begin, per_head, t_first, head_bytes, cp, w, lane};
-  if (total > 0) issue_item<D>(src, smem, rowv, 0, 0);
+  if (total > 0) issue_item<D>(src, smq0, smg0, rowv, 0, 0);
   __builtin_amdgcn_s_waitcnt(0x0F70);
   __syncthreads();
 
@@ -429,77 +522,16 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(
     for (int u = 0; u < 2; ++u) {
       const int item = i0 + u;
       if (item >= total) break;
-      if (item + 1 < total) issue_item<D>(src, smem, rowv, item + 1, 1 - u);
+      if (item + 1 < total) issue_item<D>(src, u ? smq0 : smq1, u ? smg0 : smg1, rowv, item + 1, 1 - u);
       const int r0 = (t_first + item % per_head) * kTile;
       // causal: a tile whose last row precedes the wave's first key adds nothing
       const bool skip = CAUSAL && (r0 + kTile - 1 < kw0);
-      if (!skip) {
-        const uint8_t* qb_ = smem + u * L::TBYTES;
-        const uint8_t* gb_ = smem + (2 + u) * L::TBYTES;
-        const bool need_mask = (CAUSAL && r0 < kw0 + kWaveRows - 1) || (r0 + kTile > N);
-#pragma unroll
-        for (int rb = 0; rb < 2; ++rb) {
-          // S = Q K^T and dP = dO V^T for rows rb*32 + 8(r/4) + 4hi + r%4 of the tile
-          f32x16 s, dp;
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            s[r] = 0.f;
-            dp[r] = 0.f;
-          }
-#pragma unroll
-          for (int kk = 0; kk < KK; ++kk) {
-            const bf16x8 qa = *reinterpret_cast<const bf16x8*>(qb_ + rb * 32 * L::ROWB + roff[kk]);
-            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[kk], s, 0, 0, 0);
-          }
-#pragma unroll
-          for (int kk = 0; kk < KK; ++kk) {
-            const bf16x8 ga = *reinterpret_cast<const bf16x8*>(gb_ + rb * 32 * L::ROWB + roff[kk]);
-            dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga, vf[kk], dp, 0, 0, 0);
-          }
-          sched_reads_ahead<2 * KK, 1, 2, kAhead>();
-          // P and dS for the lane's key and 16 rows; row values from LDS, 4 rows per read
-          bf16x8 pb[2], dsb[2];
-#pragma unroll
-          for (int s2 = 0; s2 < 2; ++s2) {
-            u32x4 pk, dk;
-#pragma unroll
-            for (int q4 = 0; q4 < 2; ++q4) {
-              const int rr = rb * 32 + 16 * s2 + 8 * q4 + 4 * hi;  // first of 4 consecutive rows
-              const f32x4 lv = *reinterpret_cast<const f32x4*>(&rowv[u][0][rr]);
-              const f32x4 dv = *reinterpret_cast<const f32x4*>(&rowv[u][1][rr]);
-              float pv[4], dsv[4];
-#pragma unroll
-              for (int i = 0; i < 4; ++i) {
-                const int r = 8 * s2 + 4 * q4 + i;  // accumulator index of row rr + i
-                float p = exp2_fast(__builtin_fmaf(s[r], cs, -lv[i] * kLog2e));
-                const int row = r0 + rr + i;
-                if (need_mask && ((CAUSAL && key > row) || row >= N)) p = 0.f;
-                pv[i] = p;
-                dsv[i] = p * (dp[r] - dv[i]);
-              }
-              pk[2 * q4] = pack_bf16x2(pv[0], pv[1]);
-              pk[2 * q4 + 1] = pack_bf16x2(pv[2], pv[3]);
-              dk[2 * q4] = pack_bf16x2(dsv[0], dsv[1]);
-              dk[2 * q4 + 1] = pack_bf16x2(dsv[2], dsv[3]);
-            }
-            pb[s2] = __builtin_bit_cast(bf16x8, pk);
-            dsb[s2] = __builtin_bit_cast(bf16x8, dk);
-          }
-          // dV += P^T dO, dK += dS^T Q over the 32 rows (two 16-row steps)
-          __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-          for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-            for (int db = 0; db < DB; ++db) {
-              const int r0g = (rb * 32 + 16 * s2) * L::ROWB;
-              dva[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pb[s2], tr_frag(gb_ + r0g, tlo[db], thi[db]), dva[db],
-                                                                0, 0, 0);
-              dka[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dsb[s2], tr_frag(qb_ + r0g, tlo[db], thi[db]), dka[db],
-                                                                0, 0, 0);
-            }
-          sched_reads_ahead<4 * DB, 2, 3, kAhead>();
-        }
-      }
+      // restrict LDS pointers at d = 128 (see the tile buffers above)
+      using RP = std::conditional_t<kSplitBufs, const uint8_t* __restrict__, const uint8_t*>;
+      using RF = std::conditional_t<kSplitBufs, const float* __restrict__, const float*>;
+      if (!skip)
+        dkdv_tile<D, CAUSAL, RP, RF>(u ? smq1 : smq0, u ? smg1 : smg0, rowv[u][0], rowv[u][1], r0, kw0, key, N, hi, cs,
+                                     roff, tlo, thi, kf, vf, dka, dva);
       __builtin_amdgcn_s_waitcnt(0x0F70);
       __syncthreads();
     }
