@@ -376,7 +376,9 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void fwd_bf16_kernel(
   const int g = h / G;
 
   const int tid = threadIdx.x;
-  const int w = tid >> 6;
+  // paged: a wave-uniform index keeps the page-table reads scalar (a vector load
+  // would be waited for behind the HBM -> LDS copies still in flight)
+  const int w = PAGED ? __builtin_amdgcn_readfirstlane(tid >> 6) : tid >> 6;
   const int lane = tid & 63;
   const int l32 = lane & 31;
   const int hi = lane >> 5;  // which half of the wave
