@@ -66,6 +66,10 @@ SMALL = [
     (2, 2, 1, 333, 64, False, "bf16"),
     (1, 2, 1, 513, 64, True, "bf16"),
     (1, 8, 1, 300, 128, True, "bf16"),
+    # grids with both XCD-grouped items and a plain-order tail (GQA group 4: 40 blocks;
+    # MQA group 16: 288 blocks)
+    (1, 8, 2, 1100, 128, True, "bf16"),
+    (2, 16, 1, 2100, 64, False, "bf16"),
     (1, 1, 1, 1024, 128, True, "bf16"),
     (1, 1, 1, 256, 64, False, "f32"),
     (1, 2, 1, 130, 128, True, "f32"),
