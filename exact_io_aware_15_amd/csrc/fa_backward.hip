@@ -53,8 +53,14 @@ struct BLay {
   static constexpr int TBYTES = kTile * ROWB;     // one tile
   static constexpr int BPW = TBYTES / 1024 / W;  // 1 KB blocks copied per wave (W waves)
   static_assert(BPW * W * 1024 == TBYTES, "tile copy must split evenly over the waves");
-  // physical chunk = logical chunk ^ swz(row); depends on row & 15 only
-  __host__ __device__ static constexpr int swz(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
+  // physical chunk = logical chunk ^ swz(row); depends on row & 15 only.  Tiles are
+  // read both ways: by rows (b128, 16 consecutive rows at one logical chunk: swz must
+  // be one-to-one over those rows, per LDS bank half at d = 64) and transposed (per
+  // 32-lane half, 4 consecutive rows x one aligned 4-chunk window: swz must move each
+  // of the 4 rows, per bank half at d = 64, to a different window).
+  __host__ __device__ static constexpr int swz(int r) {
+    return D == 128 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
+  }
 };
 
 typedef short s16x8 __attribute__((ext_vector_type(8)));
