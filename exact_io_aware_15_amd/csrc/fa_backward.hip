@@ -165,9 +165,11 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(const uint16_t* __restri
 // ---------------------------------------------------------------------------
 // dQ: one workgroup per (128-row query block, query head, batch), four waves of 32
 // rows.  K and V tiles of 64 keys stream through LDS (two buffers each).
-// LDS reads kept ahead of the MFMAs (measured: deeper pays off at d = 64)
+// LDS reads kept ahead of the MFMAs (measured per kernel and head dim)
 template <int D>
-constexpr int ahead_for() { return D == 64 ? 6 : 2; }
+constexpr int ahead_dq() { return D == 64 ? 6 : 4; }
+template <int D>
+constexpr int ahead_dkdv() { return D == 64 ? 6 : 2; }
 
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kDqWaves * 64, 1) void bwd_dq_kernel(
@@ -176,7 +178,7 @@ __global__ __launch_bounds__(kDqWaves * 64, 1) void bwd_dq_kernel(
     uint16_t* __restrict__ dQ, int B, int Hq, int Hkv, int N, float cs /* scale * log2 e */, float scale) {
   using L = BLay<D, kDqWaves>;
   constexpr int KK = D / 16, DB = D / 32;
-  constexpr int kAhead = ahead_for<D>();
+  constexpr int kAhead = ahead_dq<D>();
   __shared__ __attribute__((aligned(16))) uint8_t smem[4 * L::TBYTES];  // K[2], V[2]
 
   const int nqb = (N + kDqRows - 1) / kDqRows;
@@ -372,7 +374,7 @@ __device__ __forceinline__ void dkdv_tile(RP qb_, RP gb_, RF lrow, RF drow, int 
                                           const bf16x8 (&vf)[D / 16], f32x16 (&dka)[D / 32], f32x16 (&dva)[D / 32]) {
   using L = BLay<D>;
   constexpr int KK = D / 16, DB = D / 32;
-  constexpr int kAhead = ahead_for<D>();
+  constexpr int kAhead = ahead_dkdv<D>();
   const bool need_mask = (CAUSAL && r0 < kw0 + kWaveRows - 1) || (r0 + kTile > N);
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb) {
@@ -450,7 +452,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(
     int B, int Hq, int Hkv, int N, int heads_per_chunk, int nchunks, float cs, float scale) {
   using L = BLay<D>;
   constexpr int KK = D / 16, DB = D / 32;
-  constexpr int kAhead = ahead_for<D>();
+  constexpr int kAhead = ahead_dkdv<D>();
   // Q and dO tiles, two buffers each.  At d = 128 the four are separate arrays, so the
   // compiler can tell a tile's reads from the next item's copies into the other
   // buffers and does not wait for those copies mid-tile; at d = 64 one array (with
