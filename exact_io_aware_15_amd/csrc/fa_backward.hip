@@ -13,9 +13,8 @@
 //   dQ  = scale * dS K                       (bwd_dq_kernel: one pass over K/V per query block)
 //   dV  = P^T dO,   dK = scale * dS^T Q      (bwd_dkdv_kernel: one pass over Q/dO per key block)
 //
-// Both main kernels run one 64-lane wave per SIMD (four per workgroup, 512
-// registers each) and stream the other operand in 64-row tiles through two LDS
-// buffers, copied HBM -> LDS with the LDS-destination bit of 128-bit buffer loads
+// Both main kernels run eight waves per workgroup (two per SIMD) and stream the
+// other operand in 64-row tiles through two LDS buffers, copied HBM -> LDS with the LDS-destination bit of 128-bit buffer loads
 // (rows past N read as zero), rows unpadded with XOR-swizzled 16-byte chunks.
 // Every product runs on v_mfma_f32_32x32x16_bf16 with fp32 accumulation.  The dQ
 // kernel computes S^T and dP^T with a lane per query row (so the row's L and D sit
@@ -34,8 +33,9 @@
 namespace fa {
 namespace {
 
-constexpr int kBwdWaves = 4;                 // dK/dV: one wave per SIMD
-constexpr int kBwdThreads = kBwdWaves * 64;
+constexpr int kBwdWaves = 4;                 // dK/dV: key groups of 32 per workgroup
+constexpr int kKvWaves = 8;                  // dK/dV waves: two per key group (row halves), two per SIMD
+constexpr int kBwdThreads = kKvWaves * 64;
 #ifndef FA_BWD_DQ_WAVES
 #define FA_BWD_DQ_WAVES 8
 #endif
@@ -357,8 +357,8 @@ __device__ __forceinline__ void issue_item(const ItemSrc& s, uint8_t* qdst, uint
   const int h = s.h_begin + item / s.per_head;
   const int r0 = (s.t_first + item % s.per_head) * kTile;
   const size_t qo = (size_t)(s.b * s.Hq + h) * s.N;
-  copy_tile<D>(qdst, s.Q + qo * D, s.head_bytes, s.cp, r0, s.w);
-  copy_tile<D>(gdst, s.dO + qo * D, s.head_bytes, s.cp, r0, s.w);
+  copy_tile<D, kKvWaves>(qdst, s.Q + qo * D, s.head_bytes, s.cp, r0, s.w);
+  copy_tile<D, kKvWaves>(gdst, s.dO + qo * D, s.head_bytes, s.cp, r0, s.w);
   if (s.w == 0) copy_rowvals(rowv[buf][0], s.Lse + qo, s.N, r0, s.lane);
   if (s.w == 1) copy_rowvals(rowv[buf][1], s.Dlt + qo, s.N, r0, s.lane);
 }
@@ -368,16 +368,15 @@ __device__ __forceinline__ void issue_item(const ItemSrc& s, uint8_t* qdst, uint
 // dV += P^T dO and dK += dS^T Q.  RP / RF are the LDS pointer types (restrict or
 // plain, chosen by the kernel).
 template <int D, bool CAUSAL, typename RP, typename RF>
-__device__ __forceinline__ void dkdv_tile(RP qb_, RP gb_, RF lrow, RF drow, int r0, int kw0, int key, int N, int hi,
+__device__ __forceinline__ void dkdv_tile(RP qb_, RP gb_, RF lrow, RF drow, int rb, int r0, int kw0, int key, int N, int hi,
                                           float cs, const int (&roff)[D / 16], const int (&tlo)[D / 32],
                                           const int (&thi)[D / 32], const bf16x8 (&kf)[D / 16],
                                           const bf16x8 (&vf)[D / 16], f32x16 (&dka)[D / 32], f32x16 (&dva)[D / 32]) {
   using L = BLay<D>;
   constexpr int KK = D / 16, DB = D / 32;
   constexpr int kAhead = ahead_dkdv<D>();
-  const bool need_mask = (CAUSAL && r0 < kw0 + kWaveRows - 1) || (r0 + kTile > N);
-#pragma unroll
-  for (int rb = 0; rb < 2; ++rb) {
+  const bool need_mask = (CAUSAL && r0 + rb * 32 < kw0 + kWaveRows - 1) || (r0 + rb * 32 + 32 > N);
+  {
     // S = Q K^T and dP = dO V^T for rows rb*32 + 8(r/4) + 4hi + r%4 of the tile
     f32x16 s, dp;
 #pragma unroll
@@ -442,8 +441,10 @@ __device__ __forceinline__ void dkdv_tile(RP qb_, RP gb_, RF lrow, RF drow, int 
 
 // ---------------------------------------------------------------------------
 // dK, dV: one workgroup per (128-key block, K/V head, batch, chunk of the group's
-// query heads), four waves of 32 keys.  For every query head of the chunk, Q and
-// dO tiles of 64 rows (and the rows' L and D) stream through LDS (two buffers).
+// query heads), four key groups of 32 keys with two waves each: the waves of a
+// group take the two 32-row halves of every 64-row tile and keep partial dK, dV,
+// summed through LDS at the end.  For every query head of the chunk, Q and dO tiles
+// of 64 rows (and the rows' L and D) stream through LDS (two buffers).
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
@@ -480,8 +481,10 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int kg = w & (kBwdWaves - 1);  // key group
+  const int rh = w / kBwdWaves;        // row half of every 64-row tile
   const int lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
-  const int kw0 = kb * kBlockRows + w * kWaveRows;  // this wave's first key
+  const int kw0 = kb * kBlockRows + kg * kWaveRows;  // this wave's first key
   const int key = kw0 + l32;
 
   const size_t kvoff = (size_t)(b * Hkv + g) * N;
@@ -511,7 +514,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(
   for (int kk = 0; kk < KK; ++kk) roff[kk] = l32 * L::ROWB + (((2 * kk + hi) ^ L::swz(l32)) << 4);
   int tlo[DB], thi[DB];
   tr_offsets<D>(lane, tlo, thi);
-  const uint32_t cp = copy_offset<D>(w, lane);
+  const uint32_t cp = copy_offset<D, kKvWaves>(w, lane);
   const uint32_t head_bytes = (uint32_t)N * D * 2;
 
   // (head, row tile) items in order; causal: rows before the block's first key are skipped
@@ -533,18 +536,39 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(
       if (item + 1 < total) issue_item<D>(src, u ? smq0 : smq1, u ? smg0 : smg1, rowv, item + 1, 1 - u);
       const int r0 = (t_first + item % per_head) * kTile;
       // causal: a tile whose last row precedes the wave's first key adds nothing
-      const bool skip = CAUSAL && (r0 + kTile - 1 < kw0);
+      const bool skip = CAUSAL && (r0 + rh * 32 + 31 < kw0);
       // restrict LDS pointers at d = 128 (see the tile buffers above)
       using RP = std::conditional_t<kSplitBufs, const uint8_t* __restrict__, const uint8_t*>;
       using RF = std::conditional_t<kSplitBufs, const float* __restrict__, const float*>;
       if (!skip)
-        dkdv_tile<D, CAUSAL, RP, RF>(u ? smq1 : smq0, u ? smg1 : smg0, rowv[u][0], rowv[u][1], r0, kw0, key, N, hi, cs,
-                                     roff, tlo, thi, kf, vf, dka, dva);
+        dkdv_tile<D, CAUSAL, RP, RF>(u ? smq1 : smq0, u ? smg1 : smg0, rowv[u][0], rowv[u][1], rh, r0, kw0, key, N, hi,
+                                     cs, roff, tlo, thi, kf, vf, dka, dva);
       __builtin_amdgcn_s_waitcnt(0x0F70);
       __syncthreads();
     }
   }
 
+  // the two row halves of each key group are summed through LDS (the first tile
+  // buffer is free now: 16 KB per pass, one 32-column block of dK or dV per pass);
+  // the first half writes
+  {
+    float* rbuf = reinterpret_cast<float*>(sm0);
+#pragma unroll
+    for (int pass = 0; pass < 2 * DB; ++pass) {
+      f32x16& acc = pass < DB ? dka[pass] : dva[pass - DB];
+      if (rh == 1) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) rbuf[(kg * 16 + r) * 64 + lane] = acc[r];
+      }
+      __syncthreads();
+      if (rh == 0) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[r] += rbuf[(kg * 16 + r) * 64 + lane];
+      }
+      __syncthreads();
+    }
+  }
+  if (rh != 0) return;
   // lane holds keys kw0 + 8(r/4) + 4hi + r%4 at d = db*32 + l32
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
