@@ -32,6 +32,8 @@
 namespace fa {
 namespace {
 
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
 constexpr int kPage = 16;
 constexpr int kDecWaves = 4;
 constexpr int kDecThreads = kDecWaves * 64;
@@ -302,12 +304,13 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
 // (page, K/V head, token, 32 consecutive channels); the value is int8 * scale.
 // Same grid, page-id register and ping-pong buffers as decode_split_kernel; lane
 // l holds tokens 2(l/8), 2(l/8)+1 and channels (l%8)*CH .. +CH (one 32-channel
-// group), CH = D/8.  Bytes are read as b + 128 (v_cvt_f32_ubyte after flipping
-// the sign bit) and the offset is removed algebraically: q.k = sum q_c (b_c + 128)
-// - 128 sum q_c, and O += p s (b + 128) - 128 p s per group.  Both products run as
-// bf16 pair dot products (the offset bytes 1 .. 255 are exact in bf16); p s enters P V
-// rounded to bf16 and O is normalised by the sum of the rounded probabilities, L by
-// the fp32 sum.
+// group), CH = D/8.  The offsets are removed algebraically.
+//  - Keys: byte b enters as the fp16 value 1024 + (b + 128), built by one byte permute per channel pair (b ^ 0x80 as the
+//    low byte under a 0x64 high byte), against q converted exactly to fp16 under a power-of-two scale per head.  Then
+//    q.k = sum q_c (1152 + b_c) - 1152 sum q_c, with fp16 pair dot products and fp32 sums (the products are exact).
+//  - Values: byte b enters as the bf16 value b + 128 (exact for 1 .. 255), so O += p s (b + 128) - 128 p s per group,
+//    with bf16 pair dot products.  p s enters P V rounded to bf16, and O is normalised by the sum of the rounded
+//    probabilities, L by the fp32 sum.  (fp16 would bound p s to its range, which arbitrary scales need not respect.)
 template <int CH>
 struct I8Vec;
 template <>
@@ -353,26 +356,44 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_int8_kernel(
   const int dg = lane & 7;
   const int grp = dg * CH / 32;       // the lane's scale group
 
-  // q as bf16 channel pairs (dot2 operands) for the lane's channels, and 128 * sum q
-  // (the byte offset correction)
+  // q as fp16 channel pairs (the score dot2 operands) for the lane's channels.  Each
+  // head's q is scaled by a power of two that puts its largest magnitude in
+  // [2^13, 2^14), so every bf16 value converts to fp16 exactly (11 significant bits),
+  // and the score is scaled back by qunscale.  qsum = 1152 * sum q removes the key
+  // offset (see below).
   uint32_t qp[HB][CH / 2];
-  float qsum[HB];
+  float qsum[HB], qunscale[HB];
 #pragma unroll
   for (int hh = 0; hh < HB; ++hh) {
     const int hl = hb * HB + hh;
     const bool ok = hl < G;
     const uint16_t* qrow = Q + ((size_t)s * Hq + g * G + (ok ? hl : 0)) * D + dg * CH;
-    float sum = 0.f;
+    uint32_t raw[CH / 2];
+    float mx = 0.f;
 #pragma unroll
     for (int e = 0; e < CH / 8; ++e) {
       const u32x4 x = ldg16(qrow + e * 8);
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        qp[hh][e * 4 + k] = ok ? x[k] : 0u;
-        sum += ok ? bf16lo_to_f32(x[k]) + bf16hi_to_f32(x[k]) : 0.f;
+        raw[e * 4 + k] = ok ? x[k] : 0u;
+        mx = fmaxf(mx, fmaxf(fabsf(bf16lo_to_f32(raw[e * 4 + k])), fabsf(bf16hi_to_f32(raw[e * 4 + k]))));
       }
     }
-    qsum[hh] = 128.f * sum;
+    mx = fmaxf(mx, dpp<0xB1>(mx));  // max over the head's 8 channel-group lanes
+    mx = fmaxf(mx, dpp<0x4E>(mx));
+    mx = fmaxf(mx, dpp<0x141>(mx));
+    const int ex = min(max(__builtin_amdgcn_frexp_expf(mx), -100), 128);  // mx in [2^(ex-1), 2^ex)
+    const float up = ldexpf(1.f, 14 - ex);
+    qunscale[hh] = ldexpf(1.f, ex - 14);
+    float sum = 0.f;
+#pragma unroll
+    for (int i = 0; i < CH / 2; ++i) {
+      const f32x2 v = {bf16lo_to_f32(raw[i]) * up, bf16hi_to_f32(raw[i]) * up};
+      const f16x2 h = __builtin_convertvector(v, f16x2);
+      qp[hh][i] = __builtin_bit_cast(uint32_t, h);
+      sum += (float)h[0] + (float)h[1];
+    }
+    qsum[hh] = 1152.f * sum;
   }
 
   // running max, sums of the fp32 probabilities (L) and of their bf16 roundings (O),
@@ -429,21 +450,24 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_int8_kernel(
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const bool valid = (p + pp) * kPage + 2 * tg + j < n && p + pp < p_end;
-        // byte + 128 (1 .. 255, exact in bf16) as bf16 channel pairs
+        // key byte b as the fp16 value 1024 + (b + 128): the unsigned byte b ^ 0x80
+        // becomes the low byte of an fp16 whose high byte is 0x64 (one byte permute per
+        // channel pair); the products with fp16 q are exact in the fp32 sums
         uint32_t up[CH / 2];
 #pragma unroll
         for (int e = 0; e < NW; ++e) {
           const uint32_t x = kc[pp][j][e] ^ 0x80808080u;
-          up[2 * e] = pack_bf16x2((float)(x & 0xffu), (float)((x >> 8) & 0xffu));
-          up[2 * e + 1] = pack_bf16x2((float)((x >> 16) & 0xffu), (float)(x >> 24));
+          up[2 * e] = __builtin_amdgcn_perm(0x64646464u, x, 0x04010400u);
+          up[2 * e + 1] = __builtin_amdgcn_perm(0x64646464u, x, 0x04030402u);
         }
 #pragma unroll
         for (int hh = 0; hh < HB; ++hh) {
           float part = -qsum[hh];
 #pragma unroll
           for (int i = 0; i < CH / 2; ++i)
-            part = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(qp[hh][i]), as_bf16x2(up[i]), part, false);
-          part = sum8(part * ksc[pp][j]) * c;
+            part = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, qp[hh][i]), __builtin_bit_cast(f16x2, up[i]), part,
+                                          false);
+          part = sum8(part * ksc[pp][j]) * (c * qunscale[hh]);
           sc[pp][j][hh] = valid ? part : -INFINITY;
         }
       }
