@@ -71,3 +71,15 @@ def test_decode_int8_full_size():
     x = make_decode_int8(64, 32, 8, 128, 1024, 16384, seed=5)
     out, lse = run(x)
     check(x, out, lse, "full size")
+
+
+def test_decode_int8_query_magnitudes():
+    # the key products run on fp16 q under a power-of-two scale per head: heads whose q
+    # is large, tiny, zero or ordinary must all match the oracle
+    say("int8 decode query magnitudes")
+    x = make_decode_int8(3, 8, 2, 128, seed=640, fixed_ctx=(300, 17, 2000))
+    q = x["q"].float()
+    factors = torch.tensor([64.0, 2.0 ** -20, 0.0, 1.0, 2.0 ** -120, 16.0, 1.0, 0.5])
+    x["q"] = (q * factors[None, :, None]).to(torch.bfloat16)
+    out, lse = run(x)
+    check(x, out, lse, "query magnitudes")
