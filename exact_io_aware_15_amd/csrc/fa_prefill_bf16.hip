@@ -157,7 +157,9 @@ __device__ __forceinline__ void maybe_rescale(WaveState<D>& st, float mt) {
 // c > 0, so their probability is exactly 0.
 // SAFE: the row may not have seen a visible key yet (m_run = -inf, possible only
 // with a sliding window); its masked scores then give exp2(-inf - 0) = 0.
-template <int D, bool SAFE = false>
+// REL: the scores already are log2-domain logits relative to the running max, so
+// the probabilities are their plain exponentials.
+template <int D, bool SAFE = false, bool REL = false>
 __device__ __forceinline__ void softmax_pack(const f32x16 (&s)[2], WaveState<D>& st, float c,
                                              bf16x8 (&pb)[2][2]) {
   const float m = (SAFE && st.m_run == -INFINITY) ? 0.f : st.m_run;
@@ -170,8 +172,9 @@ __device__ __forceinline__ void softmax_pack(const f32x16 (&s)[2], WaveState<D>&
       u32x4 pk;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const float p0 = exp2_fast(__builtin_fmaf(s[a][h2 * 8 + 2 * j], c, -m));
-        const float p1 = exp2_fast(__builtin_fmaf(s[a][h2 * 8 + 2 * j + 1], c, -m));
+        const float p0 = REL ? exp2_fast(s[a][h2 * 8 + 2 * j]) : exp2_fast(__builtin_fmaf(s[a][h2 * 8 + 2 * j], c, -m));
+        const float p1 =
+            REL ? exp2_fast(s[a][h2 * 8 + 2 * j + 1]) : exp2_fast(__builtin_fmaf(s[a][h2 * 8 + 2 * j + 1], c, -m));
         psum += p0;
         psum += p1;
         const uint32_t w2 = pack_bf16x2(p0, p1);
@@ -192,7 +195,7 @@ __device__ __forceinline__ void softmax_pack(const f32x16 (&s)[2], WaveState<D>&
 // LDS slot (every read of a slot follows the wait and barrier that end the slot's
 // copy), which lets the compiler drop the wait for all outstanding HBM -> LDS
 // copies that it would otherwise put before the first transposing V read.
-template <int D, bool MASK, bool EXT>
+template <int D, bool MASK, bool EXT, bool LIN = false>
 __device__ __forceinline__ void process_tile(WaveState<D>& st, const uint8_t* __restrict__ kb,
                                              const uint8_t* __restrict__ vb,
                                              const int (&koff)[D / 16], const int (&voff)[D / 32], int lim,
@@ -225,7 +228,43 @@ __device__ __forceinline__ void process_tile(WaveState<D>& st, const uint8_t* __
 
   // ---- online softmax
   bf16x8 pb[2][2];
-  if constexpr (EXT) {
+  if constexpr (EXT && LIN) {
+    // Causal: a visible key never lies after its row, so the ALiBi term
+    // -slope2 |i - j| = slope2 (kofs - base) is affine in the key offset.  The logits
+    // are taken relative to ref (the running max; 0 before the row's first visible
+    // key): y = s c + slope2 kofs - (slope2 base + ref).  When the max is raised they
+    // are shifted to the new one, so the probabilities are plain exp2(y).
+    const float ref = st.m_run == -INFINITY ? 0.f : st.m_run;
+    const float nb = -__builtin_fmaf(slope2, base, ref);
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int kofs = a * 32 + 8 * (r >> 2) + (r & 3);
+        const float y = __builtin_fmaf(sc[a][r], c, __builtin_fmaf(slope2, (float)kofs, nb));
+        sc[a][r] = (!MASK || (kofs <= lim && kofs >= lo)) ? y : -INFINITY;
+      }
+    const float mt = tile_rowmax<false>(sc, 0, 1.f) + ref;  // tile max in absolute units
+    const bool grow = mt > st.m_run + kRescaleThreshold;
+    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+      const float mnew = fmaxf(st.m_run, mt);
+      float alpha = exp2_fast(st.m_run - mnew);
+      if (st.m_run == -INFINITY) alpha = 0.f;
+      st.l_exact *= alpha;
+      st.l_round *= alpha;
+#pragma unroll
+      for (int db = 0; db < WaveState<D>::DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) st.oacc[db][r] *= alpha;
+      st.m_run = mnew;
+      const float sh = mnew == -INFINITY ? 0.f : mnew - ref;
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sc[a][r] -= sh;
+    }
+    softmax_pack<D, true, true>(sc, st, 1.f, pb);
+  } else if constexpr (EXT) {
 #pragma unroll
     for (int a = 0; a < 2; ++a)
 #pragma unroll
@@ -496,9 +535,9 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void fwd_bf16_kernel(
           const int lo = window > 0 ? qrowp - window + 1 - j0 - 4 * hi : -kBC;
           const float base = (float)(qrowp - j0 - 4 * hi);
           if (need_mask)
-            process_tile<D, true, true>(st, kb, vb, koff, voff, lim, l32, c, lo, base, slope2);
+            process_tile<D, true, true, CAUSAL>(st, kb, vb, koff, voff, lim, l32, c, lo, base, slope2);
           else
-            process_tile<D, false, true>(st, kb, vb, koff, voff, lim, l32, c, lo, base, slope2);
+            process_tile<D, false, true, CAUSAL>(st, kb, vb, koff, voff, lim, l32, c, lo, base, slope2);
         } else {
           if (need_mask)
             process_tile<D, true, false>(st, kb, vb, koff, voff, lim, l32, c);
