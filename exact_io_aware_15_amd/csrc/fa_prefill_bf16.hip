@@ -355,7 +355,10 @@ __device__ __forceinline__ void copy_tile_paged(uint8_t* smem, const uint16_t* k
     const int blk = w + kWaves * i;
     const int r0 = blk * LY::RPB;                 // tile row of the block's first row
     const int tp = (j0 + r0) / 16;                // logical page
-    const int valid = min(max(nk - tp * 16, 0), 16);
+    // wave-uniform by construction; kept in scalar registers so that the buffer
+    // descriptors are too (a vector clamp here made the compiler wrap every copy in
+    // a loop over distinct descriptor values)
+    const int valid = __builtin_amdgcn_readfirstlane(min(max(nk - tp * 16, 0), 16));
     const int pid = valid > 0 ? trow[tp] : 0;
     const size_t head = ((size_t)pid * Hkv + g) * 16 * D;
     const auto krs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(kpool + head), (short)0,
