@@ -25,6 +25,7 @@
 // heads of its group; when there are too few (key block, K/V head) pairs to fill
 // the GPU (multi-query), the group's heads are split into chunks whose fp32 partial
 // sums a last kernel adds up.
+#include <climits>
 #include <type_traits>
 
 #include "fa_device.h"
@@ -139,10 +140,13 @@ __device__ __forceinline__ void sched_reads_ahead() {
 }
 
 // ---------------------------------------------------------------------------
-// D = rowsum(dO * O): D/8 lanes per row, 16-byte loads, DPP reduction.
+// D = rowsum(dO * O): D/8 lanes per row, 16-byte loads, DPP reduction.  The same
+// pass writes L2 = L * log2(e), the row's logsumexp in base 2, which the dK/dV
+// kernel subtracts per element.
 template <int D>
 __global__ __launch_bounds__(256) void bwd_delta_kernel(const uint16_t* __restrict__ O, const uint16_t* __restrict__ dO,
-                                                        float* __restrict__ Dlt, long long rows) {
+                                                        const float* __restrict__ Lse, float* __restrict__ Dlt,
+                                                        float* __restrict__ L2, long long rows) {
   constexpr int LPR = D / 8;  // lanes per row: 16 (d128) or 8 (d64)
   const long long gid = (long long)blockIdx.x * 256 + threadIdx.x;
   const long long row = gid / LPR;
@@ -159,7 +163,10 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(const uint16_t* __restri
   }
   acc = sum8(acc);                         // lanes l ^ 1, 2, 4
   if (LPR == 16) acc += dpp<0x128>(acc);   // and l ^ 8 (row_ror:8 inside 16-lane rows)
-  if (row < rows && c == 0) Dlt[row] = acc;
+  if (row < rows && c == 0) {
+    Dlt[row] = acc;
+    L2[row] = Lse[row] * kLog2e;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -341,7 +348,7 @@ __global__ __launch_bounds__(kDqWaves * 64, 1) void bwd_dq_kernel(
 struct ItemSrc {
   const uint16_t* Q;
   const uint16_t* dO;
-  const float* Lse;
+  const float* L2;
   const float* Dlt;
   int b, Hq, N, h_begin, per_head, t_first;
   uint32_t head_bytes, cp;
@@ -359,61 +366,79 @@ __device__ __forceinline__ void issue_item(const ItemSrc& s, uint8_t* qdst, uint
   const size_t qo = (size_t)(s.b * s.Hq + h) * s.N;
   copy_tile<D, kKvWaves>(qdst, s.Q + qo * D, s.head_bytes, s.cp, r0, s.w);
   copy_tile<D, kKvWaves>(gdst, s.dO + qo * D, s.head_bytes, s.cp, r0, s.w);
-  if (s.w == 0) copy_rowvals(rowv[buf][0], s.Lse + qo, s.N, r0, s.lane);
+  if (s.w == 0) copy_rowvals(rowv[buf][0], s.L2 + qo, s.N, r0, s.lane);
   if (s.w == 1) copy_rowvals(rowv[buf][1], s.Dlt + qo, s.N, r0, s.lane);
 }
 
-// One streamed item (a query head's 64-row Q/dO tile with its rows' L and D) of the
-// dK/dV kernel for this wave's 32 keys: S = Q K^T, dP = dO V^T, P, dS, then
-// dV += P^T dO and dK += dS^T Q.  RP / RF are the LDS pointer types (restrict or
-// plain, chosen by the kernel).
+// One streamed item (a query head's 64-row Q/dO tile with its rows' L2 and D) of
+// the dK/dV kernel for this wave's 32 keys, rows 32*rh .. +32 of the tile (rh, the
+// wave's row half, is already in the lane offsets roff, tlo, thi and rvo): S = Q K^T,
+// dP = dO V^T, P, dS, then dV += P^T dO and dK += dS^T Q.  need_mask is set only for
+// tiles on the causal diagonal or past N.  RP / RF are the LDS pointer types
+// (restrict or plain, chosen by the kernel).
 template <int D, bool CAUSAL, typename RP, typename RF>
-__device__ __forceinline__ void dkdv_tile(RP qb_, RP gb_, RF lrow, RF drow, int rb, int r0, int kw0, int key, int N, int hi,
+__device__ __forceinline__ void dkdv_tile(RP qb_, RP gb_, RF lrow, RF drow, bool need_mask, int rbase, int kw0, int N,
                                           float cs, const int (&roff)[D / 16], const int (&tlo)[D / 32],
-                                          const int (&thi)[D / 32], const bf16x8 (&kf)[D / 16],
+                                          const int (&thi)[D / 32], int rvo, const bf16x8 (&kf)[D / 16],
                                           const bf16x8 (&vf)[D / 16], f32x16 (&dka)[D / 32], f32x16 (&dva)[D / 32]) {
   using L = BLay<D>;
   constexpr int KK = D / 16, DB = D / 32;
   constexpr int kAhead = ahead_dkdv<D>();
-  const bool need_mask = (CAUSAL && r0 + rb * 32 < kw0 + kWaveRows - 1) || (r0 + rb * 32 + 32 > N);
-  {
-    // S = Q K^T and dP = dO V^T for rows rb*32 + 8(r/4) + 4hi + r%4 of the tile
-    f32x16 s, dp;
+  const int lane = (int)__lane_id(), l32 = lane & 31, hi = lane >> 5;
+  // S = Q K^T and dP = dO V^T for rows 8(r/4) + 4hi + r%4 of the half
+  f32x16 s, dp;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      s[r] = 0.f;
-      dp[r] = 0.f;
-    }
+  for (int r = 0; r < 16; ++r) {
+    s[r] = 0.f;
+    dp[r] = 0.f;
+  }
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      const bf16x8 qa = *reinterpret_cast<const bf16x8*>(qb_ + rb * 32 * L::ROWB + roff[kk]);
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[kk], s, 0, 0, 0);
-    }
+  for (int kk = 0; kk < KK; ++kk) {
+    const bf16x8 qa = *reinterpret_cast<const bf16x8*>(qb_ + roff[kk]);
+    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[kk], s, 0, 0, 0);
+  }
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      const bf16x8 ga = *reinterpret_cast<const bf16x8*>(gb_ + rb * 32 * L::ROWB + roff[kk]);
-      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga, vf[kk], dp, 0, 0, 0);
+  for (int kk = 0; kk < KK; ++kk) {
+    const bf16x8 ga = *reinterpret_cast<const bf16x8*>(gb_ + roff[kk]);
+    dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga, vf[kk], dp, 0, 0, 0);
+  }
+  sched_reads_ahead<2 * KK, 1, 2, kAhead>();
+  bf16x8 pb[2], dsb[2];
+  if constexpr (D == 64) {
+    // exponents s * cs - L2 in place (L2 = L log2 e); masked entries (key after the
+    // row, or row past N) get -inf in a branch that only diagonal and tail tiles take
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {  // rows 8j + 4hi .. +4
+      const f32x4 lv = *reinterpret_cast<const f32x4*>(reinterpret_cast<const uint8_t*>(lrow) + rvo + 32 * j);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) s[4 * j + i] = __builtin_fmaf(s[4 * j + i], cs, -lv[i]);
     }
-    sched_reads_ahead<2 * KK, 1, 2, kAhead>();
-    // P and dS for the lane's key and 16 rows; row values from LDS, 4 rows per read
-    bf16x8 pb[2], dsb[2];
+    if (need_mask) {
+      // the empty asm keeps this a branch (selected into every tile, the masking
+      // would cost four VALU operations per entry); -inf is made here rather than
+      // held in a register across the loop
+      float ninf;
+      asm volatile("v_mov_b32 %0, 0xff800000" : "=v"(ninf));
+      const int mlo = CAUSAL ? kw0 + l32 - rbase - 4 * hi : INT_MIN;
+      const int mhi = N - rbase - 4 * hi;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int c = 8 * (r / 4) + r % 4;  // row of entry r, less rbase + 4hi
+        if (c < mlo || c >= mhi) s[r] = ninf;
+      }
+    }
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2) {
       u32x4 pk, dk;
 #pragma unroll
       for (int q4 = 0; q4 < 2; ++q4) {
-        const int rr = rb * 32 + 16 * s2 + 8 * q4 + 4 * hi;  // first of 4 consecutive rows
-        const f32x4 lv = *reinterpret_cast<const f32x4*>(lrow + rr);
-        const f32x4 dv = *reinterpret_cast<const f32x4*>(drow + rr);
+        const int j = 2 * s2 + q4;
+        const f32x4 dv = *reinterpret_cast<const f32x4*>(reinterpret_cast<const uint8_t*>(drow) + rvo + 32 * j);
         float pv[4], dsv[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int r = 8 * s2 + 4 * q4 + i;  // accumulator index of row rr + i
-          float p = exp2_fast(__builtin_fmaf(s[r], cs, -lv[i] * kLog2e));
-          const int row = r0 + rr + i;
-          if (need_mask && ((CAUSAL && key > row) || row >= N)) p = 0.f;
-          pv[i] = p;
-          dsv[i] = p * (dp[r] - dv[i]);
+          pv[i] = exp2_fast(s[4 * j + i]);
+          dsv[i] = pv[i] * (dp[4 * j + i] - dv[i]);
         }
         pk[2 * q4] = pack_bf16x2(pv[0], pv[1]);
         pk[2 * q4 + 1] = pack_bf16x2(pv[2], pv[3]);
@@ -423,20 +448,47 @@ __device__ __forceinline__ void dkdv_tile(RP qb_, RP gb_, RF lrow, RF drow, int 
       pb[s2] = __builtin_bit_cast(bf16x8, pk);
       dsb[s2] = __builtin_bit_cast(bf16x8, dk);
     }
-    // dV += P^T dO, dK += dS^T Q over the 32 rows (two 16-row steps)
-    __builtin_amdgcn_sched_barrier(0);
+  } else {
+    // d = 128 has no registers to spare for values held across a branch: P and dS
+    // are made four rows at a time, the mask as a select
+    const int key = kw0 + l32;
 #pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2)
+    for (int s2 = 0; s2 < 2; ++s2) {
+      u32x4 pk, dk;
 #pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const int r0g = (rb * 32 + 16 * s2) * L::ROWB;
-        dva[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pb[s2], tr_frag(gb_ + r0g, tlo[db], thi[db]), dva[db],
-                                                          0, 0, 0);
-        dka[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dsb[s2], tr_frag(qb_ + r0g, tlo[db], thi[db]), dka[db],
-                                                          0, 0, 0);
+      for (int q4 = 0; q4 < 2; ++q4) {
+        const int j = 2 * s2 + q4;  // rows 8j + 4hi .. +4
+        const f32x4 lv = *reinterpret_cast<const f32x4*>(reinterpret_cast<const uint8_t*>(lrow) + rvo + 32 * j);
+        const f32x4 dv = *reinterpret_cast<const f32x4*>(reinterpret_cast<const uint8_t*>(drow) + rvo + 32 * j);
+        float pv[4], dsv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float p = exp2_fast(__builtin_fmaf(s[4 * j + i], cs, -lv[i]));
+          const int row = rbase + 8 * j + 4 * hi + i;
+          if (need_mask && ((CAUSAL && key > row) || row >= N)) p = 0.f;
+          pv[i] = p;
+          dsv[i] = p * (dp[4 * j + i] - dv[i]);
+        }
+        pk[2 * q4] = pack_bf16x2(pv[0], pv[1]);
+        pk[2 * q4 + 1] = pack_bf16x2(pv[2], pv[3]);
+        dk[2 * q4] = pack_bf16x2(dsv[0], dsv[1]);
+        dk[2 * q4 + 1] = pack_bf16x2(dsv[2], dsv[3]);
       }
-    sched_reads_ahead<4 * DB, 2, 3, kAhead>();
+      pb[s2] = __builtin_bit_cast(bf16x8, pk);
+      dsb[s2] = __builtin_bit_cast(bf16x8, dk);
+    }
   }
+  // dV += P^T dO, dK += dS^T Q over the 32 rows (two 16-row steps)
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const int r0g = 16 * s2 * L::ROWB;
+      dva[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pb[s2], tr_frag(gb_ + r0g, tlo[db], thi[db]), dva[db], 0, 0, 0);
+      dka[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dsb[s2], tr_frag(qb_ + r0g, tlo[db], thi[db]), dka[db], 0, 0, 0);
+    }
+  sched_reads_ahead<4 * DB, 2, 3, kAhead>();
 }
 
 // ---------------------------------------------------------------------------
@@ -448,7 +500,7 @@ __device__ __forceinline__ void dkdv_tile(RP qb_, RP gb_, RF lrow, RF drow, int 
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
-    const uint16_t* __restrict__ dO, const float* __restrict__ Lse, const float* __restrict__ Dlt,
+    const uint16_t* __restrict__ dO, const float* __restrict__ L2, const float* __restrict__ Dlt,
     uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, float* __restrict__ partK, float* __restrict__ partV,
     int B, int Hq, int Hkv, int N, int heads_per_chunk, int nchunks, float cs, float scale) {
   using L = BLay<D>;
@@ -459,6 +511,8 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(
   // buffers and does not wait for those copies mid-tile; at d = 64 one array (with
   // that wait) measured faster.
   constexpr bool kSplitBufs = D == 128;
+  // row values first: their addresses then fit the 16-bit offset of an LDS read
+  __shared__ __attribute__((aligned(16))) float rowv[2][2][kTile];  // [buffer][L2, D][row]
   __shared__ __attribute__((aligned(16))) uint8_t sm0[kSplitBufs ? L::TBYTES : 4 * L::TBYTES];
   __shared__ __attribute__((aligned(16))) uint8_t sm1[kSplitBufs ? L::TBYTES : 16];
   __shared__ __attribute__((aligned(16))) uint8_t sm2[kSplitBufs ? L::TBYTES : 16];
@@ -467,7 +521,6 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(
   uint8_t* const smq1 = kSplitBufs ? sm1 : sm0 + L::TBYTES;
   uint8_t* const smg0 = kSplitBufs ? sm2 : sm0 + 2 * L::TBYTES;
   uint8_t* const smg1 = kSplitBufs ? sm3 : sm0 + 3 * L::TBYTES;
-  __shared__ __attribute__((aligned(16))) float rowv[2][2][kTile];      // [buffer][L, D][row]
 
   const int G = Hq / Hkv;
   const int per_kb = B * Hkv * nchunks;
@@ -509,11 +562,20 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(
       dva[db][r] = 0.f;
     }
 
+  // lane offsets into the tiles, rows of this wave's half (adding 32 rows keeps the
+  // swizzle, which depends on the row's low four bits)
+  const int half = rh * kWaveRows * L::ROWB;
   int roff[KK];
 #pragma unroll
-  for (int kk = 0; kk < KK; ++kk) roff[kk] = l32 * L::ROWB + (((2 * kk + hi) ^ L::swz(l32)) << 4);
+  for (int kk = 0; kk < KK; ++kk) roff[kk] = half + l32 * L::ROWB + (((2 * kk + hi) ^ L::swz(l32)) << 4);
   int tlo[DB], thi[DB];
   tr_offsets<D>(lane, tlo, thi);
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+    tlo[db] += half;
+    thi[db] += half;
+  }
+  const int rvo = (rh * kWaveRows + 4 * hi) * 4;  // byte offset of the lane's first row value
   const uint32_t cp = copy_offset<D, kKvWaves>(w, lane);
   const uint32_t head_bytes = (uint32_t)N * D * 2;
 
@@ -523,7 +585,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(
   const int per_head = nt - t_first;
   const int total = nh * per_head;
 
-  const ItemSrc src{Q, dO, Lse, Dlt, b, Hq, N, h_begin, per_head, t_first, head_bytes, cp, w, lane};
+  const ItemSrc src{Q, dO, L2, Dlt, b, Hq, N, h_begin, per_head, t_first, head_bytes, cp, w, lane};
   if (total > 0) issue_item<D>(src, smq0, smg0, rowv, 0, 0);
   __builtin_amdgcn_s_waitcnt(0x0F70);
   __syncthreads();
@@ -540,9 +602,14 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(
       // restrict LDS pointers at d = 128 (see the tile buffers above)
       using RP = std::conditional_t<kSplitBufs, const uint8_t* __restrict__, const uint8_t*>;
       using RF = std::conditional_t<kSplitBufs, const float* __restrict__, const float*>;
-      if (!skip)
-        dkdv_tile<D, CAUSAL, RP, RF>(u ? smq1 : smq0, u ? smg1 : smg0, rowv[u][0], rowv[u][1], rh, r0, kw0, key, N, hi,
-                                     cs, roff, tlo, thi, kf, vf, dka, dva);
+      if (!skip) {
+        // the half's rows are r0 + 32rh + 8j + 4hi + i; the lane's entry is valid for
+        // key <= row < N
+        const int rbase = r0 + rh * kWaveRows;
+        const bool need_mask = (CAUSAL && rbase < kw0 + kWaveRows - 1) || (rbase + kWaveRows > N);
+        dkdv_tile<D, CAUSAL, RP, RF>(u ? smq1 : smq0, u ? smg1 : smg0, rowv[u][0], rowv[u][1], need_mask, rbase, kw0, N, cs,
+                                     roff, tlo, thi, rvo, kf, vf, dka, dva);
+      }
       __builtin_amdgcn_s_waitcnt(0x0F70);
       __syncthreads();
     }
@@ -609,12 +676,13 @@ hipError_t launch_bwd_t(const BwdArgs& a) {
   hipStream_t st = (hipStream_t)a.stream;
   const BwdPlan pl = bwd_plan(a.B, a.Hq, a.Hkv, a.N, a.d);
   float* dlt = (float*)a.workspace;
+  float* l2 = (float*)((uint8_t*)a.workspace + pl.l2_offset);
   float* partK = (float*)((uint8_t*)a.workspace + pl.part_offset);
   float* partV = partK + pl.part_elems;
   const long long rows = (long long)a.B * a.Hq * a.N;
   constexpr int LPR = D / 8;
   hipLaunchKernelGGL((bwd_delta_kernel<D>), dim3((unsigned)((rows * LPR + 255) / 256)), dim3(256), 0, st,
-                     (const uint16_t*)a.o, (const uint16_t*)a.dout, dlt, rows);
+                     (const uint16_t*)a.o, (const uint16_t*)a.dout, a.lse, dlt, l2, rows);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const float cs = a.scale * kLog2e;
@@ -627,7 +695,7 @@ hipError_t launch_bwd_t(const BwdArgs& a) {
   const int nkb = (a.N + kBlockRows - 1) / kBlockRows;
   hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)(nkb * a.B * a.Hkv * pl.nchunks)),
                      dim3(kBwdThreads), 0, st, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
-                     (const uint16_t*)a.dout, a.lse, dlt, (uint16_t*)a.dk, (uint16_t*)a.dv, partK, partV, a.B, a.Hq,
+                     (const uint16_t*)a.dout, l2, dlt, (uint16_t*)a.dk, (uint16_t*)a.dv, partK, partV, a.B, a.Hq,
                      a.Hkv, a.N, pl.heads_per_chunk, pl.nchunks, cs, a.scale);
   e = hipGetLastError();
   if (e != hipSuccess || pl.nchunks == 1) return e;

@@ -82,11 +82,12 @@ struct BwdArgs {
 // Backward launch plan.  dK/dV workgroups cover 128 keys of one K/V head; when
 // there are fewer than 512 of them, the query heads of each group are split into
 // chunks (each workgroup one chunk) whose fp32 partial sums are added at the end.
-// Workspace: D = rowsum(dO * O) [B][Hq][N] fp32 (padded to 256 B), then the dK and
-// dV partials [chunks][B][Hkv][N][d] fp32 each when chunks > 1.
+// Workspace: D = rowsum(dO * O) [B][Hq][N] fp32 and L2 = L * log2(e) [B][Hq][N]
+// fp32 (each padded to 256 B), then the dK and dV partials [chunks][B][Hkv][N][d]
+// fp32 each when chunks > 1.
 struct BwdPlan {
   int nchunks, heads_per_chunk;
-  size_t part_offset, part_elems, bytes;
+  size_t l2_offset, part_offset, part_elems, bytes;
 };
 inline BwdPlan bwd_plan(int B, int Hq, int Hkv, int N, int d) {
   BwdPlan p;
@@ -98,7 +99,8 @@ inline BwdPlan bwd_plan(int B, int Hq, int Hkv, int N, int d) {
   if (nch > G) nch = G;
   p.heads_per_chunk = (G + nch - 1) / nch;
   p.nchunks = (G + p.heads_per_chunk - 1) / p.heads_per_chunk;
-  p.part_offset = (((size_t)B * Hq * N * sizeof(float)) + 255) / 256 * 256;
+  p.l2_offset = (((size_t)B * Hq * N * sizeof(float)) + 255) / 256 * 256;
+  p.part_offset = 2 * p.l2_offset;
   p.part_elems = p.nchunks > 1 ? (size_t)p.nchunks * B * Hkv * N * d : 0;
   p.bytes = p.part_offset + 2 * p.part_elems * sizeof(float);
   return p;

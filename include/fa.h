@@ -129,9 +129,9 @@ int fa_prefill_paged(const void* q, const void* kpages, const void* vpages,
 
 /*
  * fa_bwd_workspace_size -- bytes of device workspace fa_bwd needs for these
- * sizes: D = rowsum(dO * O) per row (fp32), plus fp32 partial sums of dK and dV
- * when a K/V head's query heads are split over several workgroups (few K/V
- * heads).  Returns 0 when an argument is out of range.
+ * sizes: D = rowsum(dO * O) and L * log2(e) per row (fp32), plus fp32 partial
+ * sums of dK and dV when a K/V head's query heads are split over several
+ * workgroups (few K/V heads).  Returns 0 when an argument is out of range.
  */
 size_t fa_bwd_workspace_size(int B, int Hq, int Hkv, int N, int d);
 

@@ -129,10 +129,10 @@ def test_bwd_validation(L):
 
 
 def test_bwd_workspace_size(L):
-    # D per row (fp32, padded to 256 B); head-chunk partials of dK and dV only when
-    # fewer than 512 (128-key block, K/V head) pairs exist
+    # D and L log2(e) per row (fp32, each padded to 256 B); head-chunk partials of dK
+    # and dV only when fewer than 512 (128-key block, K/V head) pairs exist
     def dbytes(B, Hq, N):
-        return -(-B * Hq * N * 4 // 256) * 256
+        return 2 * (-(-B * Hq * N * 4 // 256) * 256)
     assert fa.fa_bwd_workspace_size(1, 32, 32, 8192, 128) == dbytes(1, 32, 8192)      # 2048 pairs
     assert fa.fa_bwd_workspace_size(2, 32, 8, 4096, 128) == dbytes(2, 32, 4096)       # 512 pairs
     # multi-query: 64 pairs -> 8 chunks of 4 heads
