@@ -285,9 +285,26 @@ __global__ __launch_bounds__(kDqWaves * 64, 1) void bwd_dq_kernel(
             dp[a] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, gf[kk], dp[a], 0, 0, 0);
           }
         sched_reads_ahead<4 * KK, 1, 0, kAhead>();
-        // dS^T = P^T * (dP^T - D), masked keys (after the row, or past N) give 0
+        // exponents cs * s - l2 in place; masked keys (after the row, or past N) get
+        // -inf in a branch that only tiles on the diagonal or past N take (the empty
+        // asm keeps it a branch; selected into every tile the masking would cost
+        // three VALU operations per entry)
+#pragma unroll
+        for (int a = 0; a < 2; ++a)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) s[a][r] = __builtin_fmaf(s[a][r], cs, -l2);
         const bool need_mask = CAUSAL ? (j0 + kTile - 1 > rw0) : (j0 + kTile > N);
-        const int lim = (CAUSAL ? qrow - j0 : N - 1 - j0) - 4 * hi;
+        if (need_mask) {
+          float ninf;
+          asm volatile("v_mov_b32 %0, 0xff800000" : "=v"(ninf));
+          const int lim = (CAUSAL ? qrow - j0 : N - 1 - j0) - 4 * hi;
+#pragma unroll
+          for (int a = 0; a < 2; ++a)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+              if (a * 32 + 8 * (r >> 2) + (r & 3) > lim) s[a][r] = ninf;
+        }
+        // dS^T = P^T * (dP^T - D)
         bf16x8 dsb[2][2];
 #pragma unroll
         for (int a = 0; a < 2; ++a)
@@ -300,9 +317,7 @@ __global__ __launch_bounds__(kDqWaves * 64, 1) void bwd_dq_kernel(
 #pragma unroll
               for (int e = 0; e < 2; ++e) {
                 const int r = h2 * 8 + 2 * j + e;
-                float p = exp2_fast(__builtin_fmaf(s[a][r], cs, -l2));
-                if (need_mask && a * 32 + 8 * (r >> 2) + (r & 3) > lim) p = 0.f;
-                d2[e] = p * (dp[a][r] - dl);
+                d2[e] = exp2_fast(s[a][r]) * (dp[a][r] - dl);
               }
               pk[j] = pack_bf16x2(d2[0], d2[1]);
             }
