@@ -39,6 +39,12 @@ constexpr int kDecWaves = 4;
 constexpr int kDecThreads = kDecWaves * 64;
 
 __device__ __forceinline__ u32x4 ldg16(const uint16_t* p) { return *reinterpret_cast<const u32x4*>(p); }
+// Cache pages are read exactly once per call: the loads carry the non-temporal hint
+// (global_load ... nt), so streaming them does not evict what is reused.
+template <typename T>
+__device__ __forceinline__ T ld_stream(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const T*>(p));
+}
 
 template <int D, int HB>
 __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
@@ -142,8 +148,8 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
 #pragma unroll
         for (int cc = 0; cc < CPL; ++cc) {
           const size_t off = base + (size_t)(2 * tg + j) * D + (dg + 8 * cc) * 8;
-          kd[pp][j][cc] = ldg16(KPg + off);
-          vd[pp][j][cc] = ldg16(VPg + off);
+          kd[pp][j][cc] = ld_stream<u32x4>(KPg + off);
+          vd[pp][j][cc] = ld_stream<u32x4>(VPg + off);
         }
     }
   };
@@ -436,10 +442,10 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_int8_kernel(
       for (int j = 0; j < 2; ++j) {
         const int tok = 2 * tg + j;
         const size_t off = (head * kPage + tok) * D + dg * CH;
-        kd[pp][j] = *reinterpret_cast<const vec_t*>(KQ + off);
-        vd[pp][j] = *reinterpret_cast<const vec_t*>(VQ + off);
-        ksd[pp][j] = KS[(head * kPage + tok) * NG + grp];
-        vsd[pp][j] = VS[(head * kPage + tok) * NG + grp];
+        kd[pp][j] = ld_stream<vec_t>(KQ + off);
+        vd[pp][j] = ld_stream<vec_t>(VQ + off);
+        ksd[pp][j] = ld_stream<float>(KS + (head * kPage + tok) * NG + grp);
+        vsd[pp][j] = ld_stream<float>(VS + (head * kPage + tok) * NG + grp);
       }
     }
   };
