@@ -21,7 +21,10 @@
 // in one register), like the forward, and accumulates dQ^T = K^T dS^T reading K^T
 // fragments with ds_read_b64_tr_b16.  The dK/dV kernel computes S and dP with a lane
 // per key and accumulates dV = P^T dO and dK = dS^T Q reading dO and Q through the
-// transposing reads.  Grouped query heads: a K/V head's gradients sum over the query
+// transposing reads; at d = 128 its V^T fragments come from the key block's V rows in
+// LDS.  It streams each head's unmasked row tiles first and the few that need masking
+// (the causal diagonal, the ragged end) last, each group through code of its own.
+// Grouped query heads: a K/V head's gradients sum over the query
 // heads of its group; when there are too few (key block, K/V head) pairs to fill
 // the GPU (multi-query), the group's heads are split into chunks whose fp32 partial
 // sums a last kernel adds up.
@@ -177,6 +180,10 @@ template <int D>
 constexpr int ahead_dq() { return D == 64 ? 6 : 4; }
 template <int D>
 constexpr int ahead_dkdv() { return D == 64 ? 6 : 2; }
+// dK/dV at d = 128 keeps the key block's V rows in LDS instead of registers: the 32
+// registers freed keep the kernel within its 256 without spills
+template <int D>
+constexpr bool kVinLds = D == 128;
 
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kDqWaves * 64, 1) void bwd_dq_kernel(
@@ -358,17 +365,34 @@ __global__ __launch_bounds__(kDqWaves * 64, 1) void bwd_dq_kernel(
   }
 }
 
-// Source of the dK/dV kernel's streamed items: item i is row tile
-// t_first + i % per_head of query head h_begin + i / per_head.
+// Source of the dK/dV kernel's streamed items.  Each query head of the chunk has
+// row tiles t_first .. nt-1.  Only its first n_lead tiles (on the causal diagonal of
+// the key block) and, when N is not a multiple of the tile, its last tile need masking;
+// the nu tiles between need none.  Items 0 .. n_un-1 are the unmasked tiles of every
+// head (head-major), the remaining items the nm masked tiles of every head.
 struct ItemSrc {
   const uint16_t* Q;
   const uint16_t* dO;
   const float* L2;
   const float* Dlt;
-  int b, Hq, N, h_begin, per_head, t_first;
+  int b, Hq, N, h_begin, t_first, nt, n_lead, nu, nm, n_un;
   uint32_t head_bytes, cp;
   int w, lane;
 };
+
+// (query head, row tile) of item i
+__device__ __forceinline__ void item_pos(const ItemSrc& s, int item, int& h, int& t) {
+  if (item < s.n_un) {
+    h = item / s.nu;
+    t = s.t_first + s.n_lead + item % s.nu;
+  } else {
+    const int j = item - s.n_un;
+    h = j / s.nm;
+    const int k = j % s.nm;
+    t = k < s.n_lead ? s.t_first + k : s.nt - 1;
+  }
+  h += s.h_begin;
+}
 
 // Start the HBM -> LDS copies of one item into buffer buf: its Q and dO tiles
 // (all waves) and the 64 rows' L (wave 0) and D (wave 1).
@@ -376,8 +400,9 @@ template <int D>
 __device__ __forceinline__ void issue_item(const ItemSrc& s, uint8_t* qdst, uint8_t* gdst, float (*rowv)[2][kTile],
                                            int item, int buf) {
   using L = BLay<D>;
-  const int h = s.h_begin + item / s.per_head;
-  const int r0 = (s.t_first + item % s.per_head) * kTile;
+  int h, t;
+  item_pos(s, item, h, t);
+  const int r0 = t * kTile;
   const size_t qo = (size_t)(s.b * s.Hq + h) * s.N;
   copy_tile<D, kKvWaves>(qdst, s.Q + qo * D, s.head_bytes, s.cp, r0, s.w);
   copy_tile<D, kKvWaves>(gdst, s.dO + qo * D, s.head_bytes, s.cp, r0, s.w);
@@ -388,14 +413,15 @@ __device__ __forceinline__ void issue_item(const ItemSrc& s, uint8_t* qdst, uint
 // One streamed item (a query head's 64-row Q/dO tile with its rows' L2 and D) of
 // the dK/dV kernel for this wave's 32 keys, rows 32*rh .. +32 of the tile (rh, the
 // wave's row half, is already in the lane offsets roff, tlo, thi and rvo): S = Q K^T,
-// dP = dO V^T, P, dS, then dV += P^T dO and dK += dS^T Q.  need_mask is set only for
-// tiles on the causal diagonal or past N.  RP / RF are the LDS pointer types
-// (restrict or plain, chosen by the kernel).
-template <int D, bool CAUSAL, typename RP, typename RF>
+// dP = dO V^T, P, dS, then dV += P^T dO and dK += dS^T Q.  MASK: the item may need
+// masking for some wave (need_mask: for this one); without it no masking code is
+// emitted.  RP / RF are the LDS pointer types (restrict or plain, chosen by the kernel).
+template <int D, bool CAUSAL, bool MASK, typename RP, typename RF>
 __device__ __forceinline__ void dkdv_tile(RP qb_, RP gb_, RF lrow, RF drow, bool need_mask, int rbase, int kw0, int N,
                                           float cs, const int (&roff)[D / 16], const int (&tlo)[D / 32],
                                           const int (&thi)[D / 32], int rvo, const bf16x8 (&kf)[D / 16],
-                                          const bf16x8 (&vf)[D / 16], f32x16 (&dka)[D / 32], f32x16 (&dva)[D / 32]) {
+                                          const bf16x8 (&vf)[D / 16], RP vrows, f32x16 (&dka)[D / 32],
+                                          f32x16 (&dva)[D / 32]) {
   using L = BLay<D>;
   constexpr int KK = D / 16, DB = D / 32;
   constexpr int kAhead = ahead_dkdv<D>();
@@ -415,9 +441,15 @@ __device__ __forceinline__ void dkdv_tile(RP qb_, RP gb_, RF lrow, RF drow, bool
 #pragma unroll
   for (int kk = 0; kk < KK; ++kk) {
     const bf16x8 ga = *reinterpret_cast<const bf16x8*>(gb_ + roff[kk]);
-    dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga, vf[kk], dp, 0, 0, 0);
+    // V^T fragment: from registers, or (kVinLds) from the key block's V rows in LDS
+    bf16x8 vk;
+    if constexpr (kVinLds<D>)
+      vk = *reinterpret_cast<const bf16x8*>(vrows + l32 * L::ROWB + (((2 * kk + hi) ^ L::swz(l32)) << 4));
+    else
+      vk = vf[kk];
+    dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga, vk, dp, 0, 0, 0);
   }
-  sched_reads_ahead<2 * KK, 1, 2, kAhead>();
+  sched_reads_ahead<2 * KK, kVinLds<D> ? 2 : 1, 2, kAhead>();
   bf16x8 pb[2], dsb[2];
   if constexpr (D == 64) {
     // exponents s * cs - L2 in place (L2 = L log2 e); masked entries (key after the
@@ -428,7 +460,7 @@ __device__ __forceinline__ void dkdv_tile(RP qb_, RP gb_, RF lrow, RF drow, bool
 #pragma unroll
       for (int i = 0; i < 4; ++i) s[4 * j + i] = __builtin_fmaf(s[4 * j + i], cs, -lv[i]);
     }
-    if (need_mask) {
+    if (MASK && need_mask) {
       // the empty asm keeps this a branch (selected into every tile, the masking
       // would cost four VALU operations per entry); -inf is made here rather than
       // held in a register across the loop
@@ -480,7 +512,7 @@ __device__ __forceinline__ void dkdv_tile(RP qb_, RP gb_, RF lrow, RF drow, bool
         for (int i = 0; i < 4; ++i) {
           float p = exp2_fast(__builtin_fmaf(s[4 * j + i], cs, -lv[i]));
           const int row = rbase + 8 * j + 4 * hi + i;
-          if (need_mask && ((CAUSAL && key > row) || row >= N)) p = 0.f;
+          if (MASK && need_mask && ((CAUSAL && key > row) || row >= N)) p = 0.f;
           pv[i] = p;
           dsv[i] = p * (dp[4 * j + i] - dv[i]);
         }
@@ -532,6 +564,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(
   __shared__ __attribute__((aligned(16))) uint8_t sm1[kSplitBufs ? L::TBYTES : 16];
   __shared__ __attribute__((aligned(16))) uint8_t sm2[kSplitBufs ? L::TBYTES : 16];
   __shared__ __attribute__((aligned(16))) uint8_t sm3[kSplitBufs ? L::TBYTES : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t smv[kVinLds<D> ? kBlockRows * L::ROWB : 16];  // V rows (kVinLds)
   uint8_t* const smq0 = sm0;
   uint8_t* const smq1 = kSplitBufs ? sm1 : sm0 + L::TBYTES;
   uint8_t* const smg0 = kSplitBufs ? sm2 : sm0 + 2 * L::TBYTES;
@@ -563,10 +596,23 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(
     u32x4 x = {0u, 0u, 0u, 0u}, y = {0u, 0u, 0u, 0u};
     if (key < N) {
       x = ld16(K + (kvoff + key) * D + kk * 16 + hi * 8);
-      y = ld16(V + (kvoff + key) * D + kk * 16 + hi * 8);
+      if (!kVinLds<D>) y = ld16(V + (kvoff + key) * D + kk * 16 + hi * 8);
     }
     kf[kk] = __builtin_bit_cast(bf16x8, x);
     vf[kk] = __builtin_bit_cast(bf16x8, y);
+  }
+  // kVinLds: the group's 32 V rows (key-major, 16-byte chunks swizzled like the Q
+  // tiles, so the fragment reads of 16 consecutive keys are conflict-free); each of
+  // the group's two waves stores half of the chunks.  The first barrier below orders
+  // these writes before any read.
+  if constexpr (kVinLds<D>) {
+#pragma unroll
+    for (int k2 = 0; k2 < KK / 2; ++k2) {
+      const int kk = rh * (KK / 2) + k2;
+      u32x4 y = {0u, 0u, 0u, 0u};
+      if (key < N) y = ld16(V + (kvoff + key) * D + kk * 16 + hi * 8);
+      *reinterpret_cast<u32x4*>(smv + (kg * kWaveRows + l32) * L::ROWB + (((2 * kk + hi) ^ L::swz(l32)) << 4)) = y;
+    }
   }
   f32x16 dka[DB], dva[DB];
 #pragma unroll
@@ -598,36 +644,55 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(
   const int nt = (N + kTile - 1) / kTile;
   const int t_first = CAUSAL ? (kb * kBlockRows) / kTile : 0;
   const int per_head = nt - t_first;
+  const int n_lead = CAUSAL ? min(2, per_head) : 0;
+  const int tail = (N % kTile != 0 && per_head > n_lead) ? 1 : 0;
+  const int nu = per_head - n_lead - tail, nm = n_lead + tail;
+  const int n_un = nh * nu;
   const int total = nh * per_head;
 
-  const ItemSrc src{Q, dO, L2, Dlt, b, Hq, N, h_begin, per_head, t_first, head_bytes, cp, w, lane};
+  const ItemSrc src{Q, dO, L2, Dlt, b, Hq, N, h_begin, t_first, nt, n_lead, nu, nm, n_un, head_bytes, cp, w, lane};
   if (total > 0) issue_item<D>(src, smq0, smg0, rowv, 0, 0);
   __builtin_amdgcn_s_waitcnt(0x0F70);
   __syncthreads();
 
-  for (int i0 = 0; i0 < total; i0 += 2) {
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int item = i0 + u;
-      if (item >= total) break;
-      if (item + 1 < total) issue_item<D>(src, u ? smq0 : smq1, u ? smg0 : smg1, rowv, item + 1, 1 - u);
-      const int r0 = (t_first + item % per_head) * kTile;
-      // causal: a tile whose last row precedes the wave's first key adds nothing
-      const bool skip = CAUSAL && (r0 + rh * 32 + 31 < kw0);
-      // restrict LDS pointers at d = 128 (see the tile buffers above)
-      using RP = std::conditional_t<kSplitBufs, const uint8_t* __restrict__, const uint8_t*>;
-      using RF = std::conditional_t<kSplitBufs, const float* __restrict__, const float*>;
-      if (!skip) {
-        // the half's rows are r0 + 32rh + 8j + 4hi + i; the lane's entry is valid for
-        // key <= row < N
-        const int rbase = r0 + rh * kWaveRows;
-        const bool need_mask = (CAUSAL && rbase < kw0 + kWaveRows - 1) || (rbase + kWaveRows > N);
-        dkdv_tile<D, CAUSAL, RP, RF>(u ? smq1 : smq0, u ? smg1 : smg0, rowv[u][0], rowv[u][1], need_mask, rbase, kw0, N, cs,
-                                     roff, tlo, thi, rvo, kf, vf, dka, dva);
-      }
-      __builtin_amdgcn_s_waitcnt(0x0F70);
-      __syncthreads();
+  // restrict LDS pointers at d = 128 (see the tile buffers above)
+  using RP = std::conditional_t<kSplitBufs, const uint8_t* __restrict__, const uint8_t*>;
+  using RF = std::conditional_t<kSplitBufs, const float* __restrict__, const float*>;
+  // one item in buffer u (= item parity): start the next item's copies, process this
+  // one, wait for the next to land
+  auto step = [&](auto mask_c, auto u_c, int item) {
+    constexpr bool MASK = decltype(mask_c)::value;
+    constexpr int u = decltype(u_c)::value;
+    if (item + 1 < total) issue_item<D>(src, u ? smq0 : smq1, u ? smg0 : smg1, rowv, item + 1, 1 - u);
+    int h, t;
+    item_pos(src, item, h, t);
+    const int rbase = t * kTile + rh * kWaveRows;  // the half's rows: rbase + 8j + 4hi + i
+    // causal: a tile whose last row precedes the wave's first key adds nothing (only
+    // masked items can be such tiles)
+    const bool skip = MASK && CAUSAL && (rbase + kWaveRows - 1 < kw0);
+    if (!skip) {
+      // the lane's entry is valid for key <= row < N
+      const bool need_mask = (CAUSAL && rbase < kw0 + kWaveRows - 1) || (rbase + kWaveRows > N);
+      dkdv_tile<D, CAUSAL, MASK, RP, RF>(u ? smq1 : smq0, u ? smg1 : smg0, rowv[u][0], rowv[u][1], need_mask, rbase, kw0,
+                                         N, cs, roff, tlo, thi, rvo, kf, vf, smv + kg * kWaveRows * L::ROWB, dka, dva);
     }
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+  };
+  using F = std::false_type;
+  using T = std::true_type;
+  using U0 = std::integral_constant<int, 0>;
+  using U1 = std::integral_constant<int, 1>;
+  // the unmasked items, then the masked ones (item i always uses buffer i & 1)
+  for (int i0 = 0; i0 < n_un; i0 += 2) {
+    step(F{}, U0{}, i0);
+    if (i0 + 1 < n_un) step(F{}, U1{}, i0 + 1);
+  }
+  int i1 = n_un;
+  if (i1 < total && (i1 & 1)) step(T{}, U1{}, i1++);
+  for (; i1 < total; i1 += 2) {
+    step(T{}, U0{}, i1);
+    if (i1 + 1 < total) step(T{}, U1{}, i1 + 1);
   }
 
   // the two row halves of each key group are summed through LDS (the first tile
