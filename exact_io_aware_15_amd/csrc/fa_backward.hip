@@ -179,7 +179,7 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(const uint16_t* __restri
 template <int D>
 constexpr int ahead_dq() { return D == 64 ? 6 : 4; }
 template <int D>
-constexpr int ahead_dkdv() { return D == 64 ? 6 : 2; }
+constexpr int ahead_dkdv() { return D == 64 ? 6 : 4; }
 // dK/dV at d = 128 keeps the key block's V rows in LDS instead of registers: the 32
 // registers freed keep the kernel within its 256 without spills
 template <int D>
