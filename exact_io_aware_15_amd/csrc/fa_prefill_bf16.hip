@@ -187,6 +187,15 @@ __device__ __forceinline__ void softmax_pack(const f32x16 (&s)[2], WaveState<D>&
   st.l_round += rsum;
 }
 
+// Causal ALiBi's key term as a rank-one MFMA update: A rows (keys a*32 + l32) hold
+// slope2/c times the key's offset in the tile, split into three bf16 parts (k = 0..2),
+// and B columns hold ones there, so the product adds slope2 * offset / c to every
+// score of that key.  Lanes of the upper half hold zeros (k = 8..15).
+struct AlibiExt {
+  bf16x8 a[2];
+  bf16x8 b;
+};
+
 // EXT: sliding window and/or ALiBi.  The scores are first turned into log2-domain
 // logits x = s*c - slope2*|i - j| (slope2 = ALiBi slope * log2 e; base = i - j0 - 4hi,
 // so i - j = base - koff), masked on both sides (lo <= koff <= lim), then fed to
@@ -199,7 +208,8 @@ template <int D, bool MASK, bool EXT, bool LIN = false>
 __device__ __forceinline__ void process_tile(WaveState<D>& st, const uint8_t* __restrict__ kb,
                                              const uint8_t* __restrict__ vb,
                                              const int (&koff)[D / 16], const int (&voff)[D / 32], int lim,
-                                             int l32, float c, int lo = 0, float base = 0.f, float slope2 = 0.f) {
+                                             int l32, float c, int lo = 0, float base = 0.f, float slope2 = 0.f,
+                                             const AlibiExt* ax = nullptr) {
   using LY = Lay<D>;
   constexpr int KK = D / 16;
   constexpr int DB = D / 32;
@@ -210,6 +220,10 @@ __device__ __forceinline__ void process_tile(WaveState<D>& st, const uint8_t* __
   for (int a = 0; a < 2; ++a)
 #pragma unroll
     for (int r = 0; r < 16; ++r) sc[a][r] = 0.f;
+  if constexpr (EXT && LIN) {
+#pragma unroll
+    for (int a = 0; a < 2; ++a) sc[a] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ax->a[a], ax->b, sc[a], 0, 0, 0);
+  }
 #pragma unroll
   for (int kk = 0; kk < KK; ++kk)
 #pragma unroll
@@ -218,6 +232,7 @@ __device__ __forceinline__ void process_tile(WaveState<D>& st, const uint8_t* __
       sc[a] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, st.qf[kk], sc[a], 0, 0, 0);
     }
   // schedule: kPrefetch fragment reads in flight ahead of the MFMA that consumes them
+  if constexpr (EXT && LIN) __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // the ALiBi updates first
   __builtin_amdgcn_sched_group_barrier(0x100, kPrefetch, 0);  // LDS reads
 #pragma unroll
   for (int i = 0; i < 2 * KK - kPrefetch; ++i) {
@@ -230,18 +245,19 @@ __device__ __forceinline__ void process_tile(WaveState<D>& st, const uint8_t* __
   bf16x8 pb[2][2];
   if constexpr (EXT && LIN) {
     // Causal: a visible key never lies after its row, so the ALiBi term
-    // -slope2 |i - j| = slope2 (kofs - base) is affine in the key offset.  The logits
-    // are taken relative to ref (the running max; 0 before the row's first visible
-    // key): y = s c + slope2 kofs - (slope2 base + ref).  When the max is raised they
-    // are shifted to the new one, so the probabilities are plain exp2(y).
+    // -slope2 |i - j| = slope2 (kofs + 4hi) - slope2 (base + 4hi) is affine in the key
+    // offset.  The MFMA update above already added slope2 (kofs + 4hi) / c to the
+    // scores.  The logits are taken relative to ref (the running max; 0 before the
+    // row's first visible key): y = s' c - (slope2 (base + 4hi) + ref).  When the max
+    // is raised they are shifted to the new one, so the probabilities are plain exp2(y).
     const float ref = st.m_run == -INFINITY ? 0.f : st.m_run;
-    const float nb = -__builtin_fmaf(slope2, base, ref);
+    const float nb = -__builtin_fmaf(slope2, base + (float)(4 * (int)(__lane_id() >> 5)), ref);
 #pragma unroll
     for (int a = 0; a < 2; ++a)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int kofs = a * 32 + 8 * (r >> 2) + (r & 3);
-        const float y = __builtin_fmaf(sc[a][r], c, __builtin_fmaf(slope2, (float)kofs, nb));
+        const float y = __builtin_fmaf(sc[a][r], c, nb);
         sc[a][r] = (!MASK || (kofs <= lim && kofs >= lo)) ? y : -INFINITY;
       }
     const float mt = tile_rowmax<false>(sc, 0, 1.f) + ref;  // tile max in absolute units
@@ -473,6 +489,30 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void fwd_bf16_kernel(
   // sliding window: tiles wholly left of the block's first row's window are never loaded
   const int t_begin = (EXT && window > 0) ? max(0, poff + qb * kBR - window + 1) / kBC : 0;
   const float slope2 = (EXT && slopes != nullptr) ? slopes[h] * kLog2e : 0.f;
+  AlibiExt ax;
+  if constexpr (EXT && CAUSAL) {
+    // slope2 / c per unit of key offset (c > 0; with a zero scale c is tiny and the
+    // scores' own term vanishes against the bias, as it does in exact arithmetic)
+    const float ks = slope2 / c;
+    auto rb = [](float x) { return __uint_as_float((uint32_t)__builtin_bit_cast(uint16_t, to_bf16(x)) << 16); };
+#pragma unroll
+    for (int a = 0; a < 2; ++a) {
+      u32x4 wv = {0u, 0u, 0u, 0u};
+      if (hi == 0) {
+        const float v = ks * (float)(a * 32 + l32);
+        const float h0 = rb(v), h1 = rb(v - h0), h2 = rb(v - h0 - h1);
+        wv[0] = pack_bf16x2(h0, h1);
+        wv[1] = pack_bf16x2(h2, 0.f);
+      }
+      ax.a[a] = __builtin_bit_cast(bf16x8, wv);
+    }
+    u32x4 wb = {0u, 0u, 0u, 0u};
+    if (hi == 0) {
+      wb[0] = pack_bf16x2(1.f, 1.f);
+      wb[1] = pack_bf16x2(1.f, 0.f);
+    }
+    ax.b = __builtin_bit_cast(bf16x8, wb);
+  }
 
   // ---- HBM -> LDS copies of one K/V tile (buffer loads with the LDS bit).  Wave w
   // copies 1 KB blocks w, w + 8, ... of each tensor; lane l of a block writes
@@ -538,9 +578,9 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void fwd_bf16_kernel(
           const int lo = window > 0 ? qrowp - window + 1 - j0 - 4 * hi : -kBC;
           const float base = (float)(qrowp - j0 - 4 * hi);
           if (need_mask)
-            process_tile<D, true, true, CAUSAL>(st, kb, vb, koff, voff, lim, l32, c, lo, base, slope2);
+            process_tile<D, true, true, CAUSAL>(st, kb, vb, koff, voff, lim, l32, c, lo, base, slope2, &ax);
           else
-            process_tile<D, false, true, CAUSAL>(st, kb, vb, koff, voff, lim, l32, c, lo, base, slope2);
+            process_tile<D, false, true, CAUSAL>(st, kb, vb, koff, voff, lim, l32, c, lo, base, slope2, &ax);
         } else {
           if (need_mask)
             process_tile<D, true, false>(st, kb, vb, koff, voff, lim, l32, c);

@@ -71,6 +71,19 @@ def test_window_alibi_small_every_element(shape):
     check(f64(out), f64(lse), Oref, Lref, str(shape))
 
 
+@pytest.mark.parametrize("scale", [0.0, -0.11, 0.3])
+@pytest.mark.parametrize("window", [0, 40])
+def test_causal_alibi_scale_edge_cases(scale, window):
+    # zero, negative and large softmax scales with causal ALiBi (with and without a
+    # window): the bias enters independently of the scale's size and sign
+    say(f"causal alibi scale={scale} window={window}")
+    x = make_prefill(1, 4, 2, 160, 128, "bf16", seed=57)
+    out, lse, slopes = run_ex(x, True, window, True, scale=scale)
+    Oref, Lref = attention_ref(f64(x["q"]), f64(x["k"]), f64(x["v"]), True, scale, window=window,
+                               alibi_slopes=slopes)
+    check(f64(out), f64(lse), Oref, Lref, f"scale={scale} window={window}")
+
+
 def test_fwd_ex_without_options_is_fa_fwd_bitwise():
     x = make_prefill(1, 4, 2, 450, 128, "bf16", seed=31)
     q, k, v = (x[n].to(DEV) for n in "qkv")
