@@ -29,8 +29,11 @@ sys.path.insert(0, ROOT)
 METRIC = "attention fwd TFLOP/s + % bf16 MFMA peak; paged decode GB/s + % HBM peak"
 PEAK_BF16_TFLOPS = 2516.6
 PEAK_HBM_GBS = 8000.0
+PEAK_F32_TFLOPS = 157.3
 PREFILL = "c3_bf16_causal_B1_H32_N8192_d128"
 DECODE = "c5_bf16_paged_decode_S64_Hq32_Hkv8_d128"
+OTHER_PREFILL = ("c1_f32_B1_H1_N256_d64", "c2_bf16_B4_H16_N2048_d64", "c4_bf16_causal_gqa_B2_Hq32_Hkv8_N4096_d128",
+                 "c4_bf16_causal_mqa_B2_Hq32_Hkv1_N4096_d128")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
@@ -164,7 +167,8 @@ def main():
                     help="oracle backward baseline on the first n query heads of batch 0")
     ap.add_argument("--cpu-decode-seqs", type=int, default=64,
                     help="oracle baseline on the first n sequences of the decode (64 = the whole workload)")
-    ap.add_argument("--only", choices=["prefill", "decode", "backward", "window", "chunked", "int8"], default=None,
+    ap.add_argument("--only", choices=["prefill", "decode", "backward", "window", "chunked", "int8", "configs"],
+                    default=None,
                     help="time one part only (for profiling runs)")
     ap.add_argument("--no-int8", action="store_true",
                     help="skip the INT8-cache decode measurement (reported beside the step)")
@@ -172,6 +176,8 @@ def main():
                     help="skip the chunked paged-prefill measurement (reported beside the step)")
     ap.add_argument("--no-window", action="store_true",
                     help="skip the sliding-window + ALiBi measurement (reported beside the step)")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip timing the forward on the other prefill configurations (reported beside the step)")
     ap.add_argument("--no-bwd", action="store_true",
                     help="skip the backward measurement (reported beside the step, not part of it)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -210,6 +216,7 @@ def main():
     run_w = args.only == "window" or (args.only is None and not args.no_window)
     run_c = args.only == "chunked" or (args.only is None and not args.no_chunked)
     run_i = args.only == "int8" or (args.only is None and not args.no_int8)
+    run_o = args.only == "configs" or (args.only is None and not args.no_configs)
 
     log("generating inputs")
     px = make_inputs(pcfg) if run_p else None
@@ -413,6 +420,42 @@ def main():
               "workload": "paged decode 64 seqs Hq32 Hkv8 d128 ctx~U[1024,16384] over an INT8 cache with fp32 "
                           "scales per 32 channels (288 B per token and K/V head instead of 512)"}
 
+    oc = None
+    if run_o:
+        # the forward on the other prefill configurations (not part of the step): fp32 N256 d64,
+        # bf16 non-causal d64, causal GQA and MQA at d128; same inputs as their parity tests
+        oc = {}
+        for name in OTHER_PREFILL:
+            ocfg = CONFIGS[name]
+            ox = make_inputs(ocfg)
+            oq, ok_, ov = (ox[n].to(dev) for n in "qkv")
+            oo = torch.empty_like(oq)
+            ol = torch.empty(oq.shape[:3], dtype=torch.float32, device=dev)
+            fwd = fa.fa_fwd_f32 if ocfg.dtype == "f32" else fa.fa_fwd
+
+            def other():
+                fwd(oq, ok_, ov, causal=ocfg.causal, scale=ocfg.scale, out=oo, lse=ol)
+
+            for _ in range(max(1, args.warmup)):
+                other()
+            torch.cuda.synchronize()
+            oev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
+            for i in range(K):
+                oev[i][0].record()
+                other()
+                oev[i][1].record()
+            torch.cuda.synchronize()
+            o_ms = sum(e[0].elapsed_time(e[1]) for e in oev) / K
+            ofl = prefill_flops(ocfg)
+            otf = ofl / (o_ms * 1e-3) / 1e12
+            peak = PEAK_F32_TFLOPS if ocfg.dtype == "f32" else PEAK_BF16_TFLOPS
+            log(f"{name} {o_ms * 1e3:.1f} us ({otf:.1f} TFLOP/s)")
+            oc[name] = {"ms": round(o_ms, 5), "TFLOP/s": round(otf, 2), "peak": peak,
+                        "frac": round(otf / peak, 4), "algorithmic_flops_per_launch": ofl,
+                        "kernel": ("fwd_f32_kernel" if ocfg.dtype == "f32" else "fwd_bf16_kernel")
+                        + f"<{ocfg.d}, {'causal' if ocfg.causal else 'non-causal'}>"}
+            del oq, ok_, ov, oo, ol
+
     res = {"metric": METRIC, "n_gpus": 1, "steps": K, "warmup": args.warmup, "ms_per_step": round(step_ms, 5),
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
            "data": "synthetic (seeded N(0,1) inputs; random page permutation)"}
@@ -451,9 +494,14 @@ def main():
         res["decode_int8"] = d8
     if bwd is not None:
         res["backward"] = bwd
+    if oc is not None:
+        res["other_configs"] = oc
     if "value" not in res:  # one of the measurements beside the step was run alone
-        one = next(x for x in (bwd, wa, cp, d8) if x is not None)
-        res.update({"value": one["value"], "unit": one["unit"], "roofline": one["roofline"]})
+        one = next((x for x in (bwd, wa, cp, d8) if x is not None), None)
+        if one is not None:
+            res.update({"value": one["value"], "unit": one["unit"], "roofline": one["roofline"]})
+        else:
+            res.update({"value": None, "unit": "TFLOP/s", "roofline": None})
     res["config"] = cfg_desc
     if not args.no_cpu_baseline:
         log("timing the fp64 CPU oracle on a bounded sample")

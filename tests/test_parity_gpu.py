@@ -100,6 +100,26 @@ def test_prefill_scale_edge_cases(scale):
         check(f64(out), f64(lse), Oref, Lref, "bf16", f"scale={scale} causal={causal}")
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("step", [0.004, 0.012, 0.05])
+def test_prefill_rising_logits(d, step):
+    """Scores that rise along the keys: q ~ 1 + 0.1 N(0,1) and key j ~ step*j + 0.1 N(0,1)
+    per channel, so each 64-key tile's scores exceed the previous tile's by about
+    sqrt(d)*step*64*log2(e) log2 units: 3-4 (the running max is kept), 9-12 (it is
+    raised on every tile) or 37-52 (exponentials against the old max overflow)."""
+    say(f"prefill rising logits d={d} step={step}")
+    N = 700
+    x = make_prefill(1, 2, 1, N, d, "bf16", seed=31 + d)
+    ramp = step * torch.arange(N, dtype=torch.float32).view(1, 1, N, 1)
+    x = dict(x)
+    x["q"] = (1.0 + 0.1 * x["q"].float()).to(torch.bfloat16)
+    x["k"] = (ramp + 0.1 * x["k"].float()).to(torch.bfloat16)
+    for causal in (False, True):
+        out, lse = gpu_prefill(x, causal, "bf16")
+        Oref, Lref = attention_ref(f64(x["q"]), f64(x["k"]), f64(x["v"]), causal, 1.0 / np.sqrt(d))
+        check(f64(out), f64(lse), Oref, Lref, "bf16", f"rising d={d} step={step} causal={causal}")
+
+
 def sample_rows(N, seed, extra=48):
     rng = np.random.default_rng(seed)
     fixed = [0, 1, 2, 3, 31, 32, 63, 64, 65, 127, 128, 255, 256, 257, 511, 512, N // 2, N - 2, N - 1]
