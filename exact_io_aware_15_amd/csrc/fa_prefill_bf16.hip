@@ -9,9 +9,9 @@
 // Work decomposition: one workgroup of 8 waves (two per SIMD) per (256-row query
 // block, query head, batch).  Each wave owns 32 query rows and keeps their Q
 // fragments in registers for the whole pass.  K/V are streamed in tiles of 64
-// keys through two LDS buffers: the next tile is copied HBM -> LDS by 128-bit
-// buffer loads with the LDS-destination bit (no staging registers; rows past N
-// read as zero) while the current one is consumed.  Rows are stored unpadded
+// keys (128 at d = 64) through two LDS buffers: the next tile is copied
+// HBM -> LDS by 128-bit buffer loads with the LDS-destination bit (no staging
+// registers; rows past N read as zero) while the current one is consumed.  Rows are stored unpadded
 // with their 16-byte chunks XOR-swizzled by row, so the b128 K reads and the
 // transposing V reads both hit distinct LDS banks.  Per tile and wave:
 //   S^T = K Q^T  with v_mfma_f32_32x32x16_bf16 (K from LDS is the A operand, so
@@ -52,7 +52,6 @@ constexpr int kRowsPerWave = 32;            // one 32-row MFMA block per wave
 constexpr int kWaves = FA_PREFILL_WAVES;    // waves per workgroup (8: two per SIMD)
 constexpr int kThreads = kWaves * 64;
 constexpr int kBR = kWaves * kRowsPerWave;  // 256 query rows per workgroup
-constexpr int kBC = 64;                     // keys per tile (two 32-key MFMA blocks)
 constexpr float kRescaleThreshold = 8.0f;   // log2 units: probabilities stay <= 256
 constexpr int kPrefetch = 4;                // LDS fragment reads kept ahead of the MFMAs
 #ifndef FA_PREFILL_STAGES
@@ -65,7 +64,12 @@ struct Lay {
   static constexpr int ROWB = D * 2;            // bytes per K/V row in LDS (unpadded)
   static constexpr int CPR = ROWB / 16;         // 16-byte chunks per row
   static constexpr int RPB = 1024 / ROWB;       // rows per 1 KB wave copy (64 lanes x 16 B)
-  static constexpr int TBYTES = kBC * ROWB;     // one tensor tile
+  // Keys per tile: 64 at d = 128 (two 32-key MFMA blocks), 128 at d = 64, where a
+  // tile's matrix work per key is half as large and the wider tile halves the
+  // barriers and copy waits per key.
+  static constexpr int BC = D == 64 ? 128 : 64;
+  static constexpr int NA = BC / 32;            // 32-key MFMA blocks per tile
+  static constexpr int TBYTES = BC * ROWB;      // one tensor tile
   static constexpr int BLOCKS = TBYTES / 1024;  // 1 KB copies per tensor tile
   static constexpr int BPW = BLOCKS / kWaves;   // ... per wave
   static_assert(BPW * kWaves == BLOCKS, "tile copy must split evenly over the waves");
@@ -114,11 +118,11 @@ struct WaveState {
 
 // Row max of one tile's scores (masked where needed), in log2 units.
 // lim: largest key offset (within the tile, minus the lane's 4*hi) that is visible.
-template <bool MASK>
-__device__ __forceinline__ float tile_rowmax(f32x16 (&s)[2], int lim, float c) {
+template <bool MASK, int NA>
+__device__ __forceinline__ float tile_rowmax(f32x16 (&s)[NA], int lim, float c) {
   float mx = -INFINITY;
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
+  for (int a = 0; a < NA; ++a)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       if (MASK) {
@@ -160,13 +164,13 @@ __device__ __forceinline__ void maybe_rescale(WaveState<D>& st, float mt) {
 // REL: the scores already are log2-domain logits relative to the running max, so
 // the probabilities are their plain exponentials.
 template <int D, bool SAFE = false, bool REL = false>
-__device__ __forceinline__ void softmax_pack(const f32x16 (&s)[2], WaveState<D>& st, float c,
-                                             bf16x8 (&pb)[2][2]) {
+__device__ __forceinline__ void softmax_pack(const f32x16 (&s)[Lay<D>::NA], WaveState<D>& st, float c,
+                                             bf16x8 (&pb)[Lay<D>::NA][2]) {
   const float m = (SAFE && st.m_run == -INFINITY) ? 0.f : st.m_run;
   const bf16x2 ones = as_bf16x2(0x3f803f80u);
   float psum = 0.f, rsum = 0.f;
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
+  for (int a = 0; a < Lay<D>::NA; ++a)
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2) {
       u32x4 pk;
@@ -192,7 +196,7 @@ __device__ __forceinline__ void softmax_pack(const f32x16 (&s)[2], WaveState<D>&
 // and B columns hold ones there, so the product adds slope2 * offset / c to every
 // score of that key.  Lanes of the upper half hold zeros (k = 8..15).
 struct AlibiExt {
-  bf16x8 a[2];
+  bf16x8 a[4];  // one per 32-key block of the tile (two or four used)
   bf16x8 b;
 };
 
@@ -213,36 +217,37 @@ __device__ __forceinline__ void process_tile(WaveState<D>& st, const uint8_t* __
   using LY = Lay<D>;
   constexpr int KK = D / 16;
   constexpr int DB = D / 32;
+  constexpr int NA = LY::NA;
 
   // ---- scores S^T = K Q^T; K fragment: key a*32 + l32, d = kk*16 + hi*8 .. +8
-  f32x16 sc[2];
+  f32x16 sc[NA];
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
+  for (int a = 0; a < NA; ++a)
 #pragma unroll
     for (int r = 0; r < 16; ++r) sc[a][r] = 0.f;
   if constexpr (EXT && LIN) {
 #pragma unroll
-    for (int a = 0; a < 2; ++a) sc[a] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ax->a[a], ax->b, sc[a], 0, 0, 0);
+    for (int a = 0; a < NA; ++a) sc[a] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ax->a[a], ax->b, sc[a], 0, 0, 0);
   }
 #pragma unroll
   for (int kk = 0; kk < KK; ++kk)
 #pragma unroll
-    for (int a = 0; a < 2; ++a) {
+    for (int a = 0; a < NA; ++a) {
       const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kb + (a * 32 + l32) * LY::ROWB + koff[kk]);
       sc[a] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, st.qf[kk], sc[a], 0, 0, 0);
     }
   // schedule: kPrefetch fragment reads in flight ahead of the MFMA that consumes them
-  if constexpr (EXT && LIN) __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // the ALiBi updates first
+  if constexpr (EXT && LIN) __builtin_amdgcn_sched_group_barrier(0x008, NA, 0);  // the ALiBi updates first
   __builtin_amdgcn_sched_group_barrier(0x100, kPrefetch, 0);  // LDS reads
 #pragma unroll
-  for (int i = 0; i < 2 * KK - kPrefetch; ++i) {
+  for (int i = 0; i < NA * KK - kPrefetch; ++i) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
     __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
   }
   __builtin_amdgcn_sched_group_barrier(0x008, kPrefetch, 0);
 
   // ---- online softmax
-  bf16x8 pb[2][2];
+  bf16x8 pb[NA][2];
   if constexpr (EXT && LIN) {
     // Causal: a visible key never lies after its row, so the ALiBi term
     // -slope2 |i - j| = slope2 (kofs + 4hi) - slope2 (base + 4hi) is affine in the key
@@ -253,7 +258,7 @@ __device__ __forceinline__ void process_tile(WaveState<D>& st, const uint8_t* __
     const float ref = st.m_run == -INFINITY ? 0.f : st.m_run;
     const float nb = -__builtin_fmaf(slope2, base + (float)(4 * (int)(__lane_id() >> 5)), ref);
 #pragma unroll
-    for (int a = 0; a < 2; ++a)
+    for (int a = 0; a < NA; ++a)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int kofs = a * 32 + 8 * (r >> 2) + (r & 3);
@@ -275,14 +280,14 @@ __device__ __forceinline__ void process_tile(WaveState<D>& st, const uint8_t* __
       st.m_run = mnew;
       const float sh = mnew == -INFINITY ? 0.f : mnew - ref;
 #pragma unroll
-      for (int a = 0; a < 2; ++a)
+      for (int a = 0; a < NA; ++a)
 #pragma unroll
         for (int r = 0; r < 16; ++r) sc[a][r] -= sh;
     }
     softmax_pack<D, true, true>(sc, st, 1.f, pb);
   } else if constexpr (EXT) {
 #pragma unroll
-    for (int a = 0; a < 2; ++a)
+    for (int a = 0; a < NA; ++a)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int kofs = a * 32 + 8 * (r >> 2) + (r & 3);
@@ -305,7 +310,7 @@ __device__ __forceinline__ void process_tile(WaveState<D>& st, const uint8_t* __
   // where their registers would push the wave past its 256-register budget)
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
+  for (int a = 0; a < NA; ++a)
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
@@ -320,7 +325,7 @@ __device__ __forceinline__ void process_tile(WaveState<D>& st, const uint8_t* __
   // same schedule for the V fragments (two transposing reads per MFMA)
   __builtin_amdgcn_sched_group_barrier(0x100, 2 * kPrefetch, 1);
 #pragma unroll
-  for (int i = 0; i < 4 * DB - kPrefetch; ++i) {
+  for (int i = 0; i < 2 * NA * DB - kPrefetch; ++i) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
     __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
   }
@@ -354,7 +359,7 @@ __device__ __forceinline__ void copy_tile(uint8_t* smem, const void* kbase, cons
 // chunk length C; sequence s holds ctxl[s] >= C cached tokens in 16-token pages
 // (K, V are the page pools [pages][Hkv][16][D], table the page table), the chunk
 // rows sit at positions ctxl[s] - C + r and the attention is causal in positions.
-// HBM -> LDS copy of one K/V tile (keys j0 .. j0+63, four 16-token pages) from the
+// HBM -> LDS copy of one K/V tile (keys j0 .. j0+BC-1, BC/16 16-token pages) from the
 // page pools, into buffer buf with the same swizzled layout as copy_tile.  Each 1 KB
 // block lies in one page (slot rows pr0 .. pr0 + RPB - 1); its buffer descriptor
 // spans only the page's valid slots (below nk), so slots past the context -- and
@@ -485,9 +490,9 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void fwd_bf16_kernel(
   }
 
   const int kend = CAUSAL ? min(Nk, poff + (qb + 1) * kBR) : Nk;
-  const int ntiles = (kend + kBC - 1) / kBC;
+  const int ntiles = (kend + LY::BC - 1) / LY::BC;
   // sliding window: tiles wholly left of the block's first row's window are never loaded
-  const int t_begin = (EXT && window > 0) ? max(0, poff + qb * kBR - window + 1) / kBC : 0;
+  const int t_begin = (EXT && window > 0) ? max(0, poff + qb * kBR - window + 1) / LY::BC : 0;
   const float slope2 = (EXT && slopes != nullptr) ? slopes[h] * kLog2e : 0.f;
   AlibiExt ax;
   if constexpr (EXT && CAUSAL) {
@@ -496,7 +501,7 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void fwd_bf16_kernel(
     const float ks = slope2 / c;
     auto rb = [](float x) { return __uint_as_float((uint32_t)__builtin_bit_cast(uint16_t, to_bf16(x)) << 16); };
 #pragma unroll
-    for (int a = 0; a < 2; ++a) {
+    for (int a = 0; a < LY::NA; ++a) {
       u32x4 wv = {0u, 0u, 0u, 0u};
       if (hi == 0) {
         const float v = ks * (float)(a * 32 + l32);
@@ -539,9 +544,9 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void fwd_bf16_kernel(
   for (int p = 0; p < kStages - 1; ++p)
     if (t_begin + p < ntiles) {
       if constexpr (PAGED)
-        copy_tile_paged<D>(smem, K, V, trow, Nk, Hkv, g, (t_begin + p) * kBC, p, w, lane);
+        copy_tile_paged<D>(smem, K, V, trow, Nk, Hkv, g, (t_begin + p) * LY::BC, p, w, lane);
       else
-        copy_tile<D>(smem, kbase, vbase, head_bytes, kcp, vcp, (t_begin + p) * kBC, p, w);
+        copy_tile<D>(smem, kbase, vbase, head_bytes, kcp, vcp, (t_begin + p) * LY::BC, p, w);
     }
   wait_vmem_tiles<kLoadsPerTile>(min(kStages - 2, ntiles - 1 - t_begin));  // the first tile has landed
   __syncthreads();
@@ -553,20 +558,20 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void fwd_bf16_kernel(
     for (int u = 0; u < kStages; ++u) {
       const int t = t0 + u;
       if (t >= ntiles) break;
-      const int j0 = t * kBC;
+      const int j0 = t * LY::BC;
       if (t + kStages - 1 < ntiles) {
         if constexpr (PAGED)
-          copy_tile_paged<D>(smem, K, V, trow, Nk, Hkv, g, j0 + (kStages - 1) * kBC, (u + kStages - 1) % kStages, w,
+          copy_tile_paged<D>(smem, K, V, trow, Nk, Hkv, g, j0 + (kStages - 1) * LY::BC, (u + kStages - 1) % kStages, w,
                              lane);
         else
-          copy_tile<D>(smem, kbase, vbase, head_bytes, kcp, vcp, j0 + (kStages - 1) * kBC,
+          copy_tile<D>(smem, kbase, vbase, head_bytes, kcp, vcp, j0 + (kStages - 1) * LY::BC,
                        (u + kStages - 1) % kStages, w);
       }
 
-      const bool left_of_window = EXT && window > 0 && (j0 + kBC - 1 < rw0p - window + 1);
+      const bool left_of_window = EXT && window > 0 && (j0 + LY::BC - 1 < rw0p - window + 1);
       const bool skip = (CAUSAL && (j0 > rw0p + kRowsPerWave - 1)) || left_of_window;
       if (!skip) {
-        const bool need_mask = (CAUSAL ? (j0 + kBC - 1 > rw0p) : (j0 + kBC > Nk)) ||
+        const bool need_mask = (CAUSAL ? (j0 + LY::BC - 1 > rw0p) : (j0 + LY::BC > Nk)) ||
                                (EXT && window > 0 && j0 < rw0p + kRowsPerWave - window);
         // causal: key j0 + koff visible iff koff + 4*hi <= qrow - j0 (keys past N
         // only reach rows >= N, which are never stored); otherwise iff key < N
@@ -575,7 +580,7 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void fwd_bf16_kernel(
         const uint8_t* vb = smem + (kStages + u) * LY::TBYTES;
         if constexpr (EXT) {
           // window: key visible iff koff + 4*hi >= qrow - window + 1 - j0
-          const int lo = window > 0 ? qrowp - window + 1 - j0 - 4 * hi : -kBC;
+          const int lo = window > 0 ? qrowp - window + 1 - j0 - 4 * hi : -LY::BC;
           const float base = (float)(qrowp - j0 - 4 * hi);
           if (need_mask)
             process_tile<D, true, true, CAUSAL>(st, kb, vb, koff, voff, lim, l32, c, lo, base, slope2, &ax);
