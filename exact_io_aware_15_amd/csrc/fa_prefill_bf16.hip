@@ -540,13 +540,20 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void fwd_bf16_kernel(
   // wave's outstanding loads in issue order), so a copy has kStages - 1 tile-times
   // to arrive from HBM.
   constexpr int kLoadsPerTile = 2 * LY::BPW;
+  // Tile order: left to right, except with causal ALiBi, whose bias grows toward
+  // the diagonal: walking the tiles from the diagonal leftward sets each row's
+  // running max on its first tile, where a left-to-right walk raises it (and
+  // rescales O) on most tiles of the steeper heads.  Loop index t then stands for
+  // the tile ntiles - 1 - (t - t_begin).
+  const bool rev = EXT && CAUSAL && slopes != nullptr;
+  constexpr int kAhead = (kStages - 1) * LY::BC;  // key distance of the tile copied ahead
 #pragma unroll
   for (int p = 0; p < kStages - 1; ++p)
     if (t_begin + p < ntiles) {
       if constexpr (PAGED)
-        copy_tile_paged<D>(smem, K, V, trow, Nk, Hkv, g, (t_begin + p) * LY::BC, p, w, lane);
+        copy_tile_paged<D>(smem, K, V, trow, Nk, Hkv, g, (rev ? ntiles - 1 - p : t_begin + p) * LY::BC, p, w, lane);
       else
-        copy_tile<D>(smem, kbase, vbase, head_bytes, kcp, vcp, (t_begin + p) * LY::BC, p, w);
+        copy_tile<D>(smem, kbase, vbase, head_bytes, kcp, vcp, (rev ? ntiles - 1 - p : t_begin + p) * LY::BC, p, w);
     }
   wait_vmem_tiles<kLoadsPerTile>(min(kStages - 2, ntiles - 1 - t_begin));  // the first tile has landed
   __syncthreads();
@@ -558,13 +565,13 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void fwd_bf16_kernel(
     for (int u = 0; u < kStages; ++u) {
       const int t = t0 + u;
       if (t >= ntiles) break;
-      const int j0 = t * LY::BC;
+      const int j0 = rev ? (ntiles - 1 - (t - t_begin)) * LY::BC : t * LY::BC;
       if (t + kStages - 1 < ntiles) {
         if constexpr (PAGED)
-          copy_tile_paged<D>(smem, K, V, trow, Nk, Hkv, g, j0 + (kStages - 1) * LY::BC, (u + kStages - 1) % kStages, w,
+          copy_tile_paged<D>(smem, K, V, trow, Nk, Hkv, g, rev ? j0 - kAhead : j0 + kAhead, (u + kStages - 1) % kStages, w,
                              lane);
         else
-          copy_tile<D>(smem, kbase, vbase, head_bytes, kcp, vcp, j0 + (kStages - 1) * LY::BC,
+          copy_tile<D>(smem, kbase, vbase, head_bytes, kcp, vcp, rev ? j0 - kAhead : j0 + kAhead,
                        (u + kStages - 1) % kStages, w);
       }
 
