@@ -135,6 +135,23 @@ __device__ __forceinline__ float tile_rowmax(f32x16 (&s)[NA], int lim, float c) 
   return mx * c;  // c > 0, so -inf stays -inf
 }
 
+// Same with the mask applied only when need_mask (wave-uniform) is set: one code
+// path for masked and unmasked tiles, so the accumulators are not copied between
+// two register assignments where the paths would rejoin.
+template <int NA>
+__device__ __forceinline__ float tile_rowmax_rt(f32x16 (&s)[NA], int lim, float c, bool need_mask) {
+  if (need_mask) {
+#pragma unroll
+    for (int a = 0; a < NA; ++a)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int koff = a * 32 + 8 * (r >> 2) + (r & 3);
+        s[a][r] = (koff <= lim) ? s[a][r] : -INFINITY;
+      }
+  }
+  return tile_rowmax<false>(s, lim, c);
+}
+
 // Raise the running max of rows whose tile max exceeds it by more than the
 // threshold, rescaling O and the sums.  Wave-uniform branch.
 // SAFE: a row may still be at m_run = -inf when another row of the wave grows (only
@@ -208,12 +225,13 @@ struct AlibiExt {
 // LDS slot (every read of a slot follows the wait and barrier that end the slot's
 // copy), which lets the compiler drop the wait for all outstanding HBM -> LDS
 // copies that it would otherwise put before the first transposing V read.
-template <int D, bool MASK, bool EXT, bool LIN = false>
+// RTMASK: plain path with the mask decided at run time by need_mask.
+template <int D, bool MASK, bool EXT, bool LIN = false, bool RTMASK = false>
 __device__ __forceinline__ void process_tile(WaveState<D>& st, const uint8_t* __restrict__ kb,
                                              const uint8_t* __restrict__ vb,
                                              const int (&koff)[D / 16], const int (&voff)[D / 32], int lim,
                                              int l32, float c, int lo = 0, float base = 0.f, float slope2 = 0.f,
-                                             const AlibiExt* ax = nullptr) {
+                                             const AlibiExt* ax = nullptr, bool need_mask = false) {
   using LY = Lay<D>;
   constexpr int KK = D / 16;
   constexpr int DB = D / 32;
@@ -298,7 +316,7 @@ __device__ __forceinline__ void process_tile(WaveState<D>& st, const uint8_t* __
     maybe_rescale<D, true>(st, mt);
     softmax_pack<D, true>(sc, st, 1.f, pb);
   } else {
-    const float mt = tile_rowmax<MASK>(sc, lim, c);
+    const float mt = RTMASK ? tile_rowmax_rt(sc, lim, c, need_mask) : tile_rowmax<MASK>(sc, lim, c);
     maybe_rescale<D>(st, mt);
     softmax_pack<D>(sc, st, c, pb);
   }
@@ -594,10 +612,15 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void fwd_bf16_kernel(
           else
             process_tile<D, false, true, CAUSAL>(st, kb, vb, koff, voff, lim, l32, c, lo, base, slope2, &ax);
         } else {
-          if (need_mask)
+          if constexpr (!CAUSAL) {
+            // only a ragged last tile is masked
+            process_tile<D, false, false, false, true>(st, kb, vb, koff, voff, lim, l32, c, 0, 0.f, 0.f, nullptr,
+                                                       need_mask);
+          } else if (need_mask) {
             process_tile<D, true, false>(st, kb, vb, koff, voff, lim, l32, c);
-          else
+          } else {
             process_tile<D, false, false>(st, kb, vb, koff, voff, lim, l32, c);
+          }
         }
       }
 
