@@ -41,6 +41,23 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+def warm(fn, n_min, ms_min=100.0):
+    """Untimed launches before a measurement beside the step: at least n_min, and at
+    least ms_min of wall time, since the GPU clock takes tens of milliseconds of load
+    to settle (a short kernel warmed by a few launches is timed at a lower clock)."""
+    import torch
+
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    i = 0
+    while i < n_min or (time.perf_counter() - t0) * 1e3 < ms_min:
+        fn()
+        i += 1
+        if i % 8 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+
+
 def source_digest(files):
     h = hashlib.sha256()
     for f in files:
@@ -158,8 +175,9 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=30,
-                    help="untimed steps first (the GPU clock takes tens of milliseconds of load to settle)")
+    ap.add_argument("--warmup", type=int, default=200,
+                    help="untimed steps first (the GPU clock takes tens of milliseconds of load to settle; "
+                         "200 steps are about 0.2 s)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-row-stride", type=int, default=1,
                     help="oracle baseline on every n-th query row of the prefill (1 = the whole workload)")
@@ -287,9 +305,7 @@ def main():
             fa.fa_bwd(bq, bk, bv, bo, bl, bdo, causal=pcfg.causal, scale=pcfg.scale, dq=bdq, dk=bdk, dv=bdv,
                       workspace=bws)
 
-        for _ in range(max(1, args.warmup // 3)):
-            backward()
-        torch.cuda.synchronize()
+        warm(backward, max(1, args.warmup // 3))
         bev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
         for i in range(K):
             bev[i][0].record()
@@ -320,9 +336,7 @@ def main():
         def windowed():
             fa.fa_fwd_ex(bq, bk, bv, causal=True, scale=pcfg.scale, window=W, alibi_slopes=slopes, out=wo, lse=wl)
 
-        for _ in range(max(1, args.warmup // 3)):
-            windowed()
-        torch.cuda.synchronize()
+        warm(windowed, max(1, args.warmup // 3))
         wev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
         for i in range(K):
             wev[i][0].record()
@@ -357,9 +371,7 @@ def main():
             fa.fa_prefill_paged(cg["q"], cg["kpages"], cg["vpages"], cg["page_table"], cg["ctx_lens"], out=co,
                                 lse=cl)
 
-        for _ in range(max(1, args.warmup // 3)):
-            chunked()
-        torch.cuda.synchronize()
+        warm(chunked, max(1, args.warmup // 3))
         cev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
         for i in range(K):
             cev[i][0].record()
@@ -396,9 +408,7 @@ def main():
             fa.fa_decode_paged_int8(ig["q"], ig["kq"], ig["kscale"], ig["vq"], ig["vscale"], ig["page_table"],
                                     ig["ctx_lens"], out=io, lse=il, workspace=iws)
 
-        for _ in range(max(1, args.warmup // 3)):
-            int8_decode()
-        torch.cuda.synchronize()
+        warm(int8_decode, max(1, args.warmup // 3))
         iev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
         for i in range(K):
             iev[i][0].record()
@@ -436,9 +446,7 @@ def main():
             def other():
                 fwd(oq, ok_, ov, causal=ocfg.causal, scale=ocfg.scale, out=oo, lse=ol)
 
-            for _ in range(max(1, args.warmup)):
-                other()
-            torch.cuda.synchronize()
+            warm(other, max(1, args.warmup // 3))
             oev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
             for i in range(K):
                 oev[i][0].record()
