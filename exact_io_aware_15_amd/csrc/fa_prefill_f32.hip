@@ -7,27 +7,46 @@
 // output accumulator that is rescaled by exp(m_old - m_new) per tile.  Causal
 // tiles entirely above the diagonal are never loaded.  Only O and L are written.
 //
-// One thread owns 64 of the d columns of one query row (d = 64: one thread per
-// row; d = 128: two threads per row that combine their partial dot products with
-// one DPP exchange).  This path exists for fp32 inputs, whose sizes in practice
-// are small; it uses VALU FMAs, not matrix cores.
+// Four waves per workgroup share each K/V tile in LDS.  Each query row is shared
+// by TPR = d/16 lanes, each owning 16 of its d columns: a dot product is 16 FMAs
+// per lane plus two (d = 64) or three (d = 128) DPP additions across the row's
+// lanes, and the P V update is 16 FMAs per lane and key.  A workgroup holds
+// 4*64/TPR rows (64 at d = 64, 32 at d = 128), and the per-lane work is a quarter
+// (an eighth) of a whole-row thread's, so short sequences still keep many waves busy.  This path exists for fp32
+// inputs, whose sizes in practice are small; it uses VALU FMAs, not matrix cores.
 #include "fa_device.h"
 #include "fa_launch.h"
 
 namespace fa {
 namespace {
 
-constexpr int kRows = 64;    // query rows per workgroup (B_r)
 constexpr int kKeys = 64;    // keys per tile (B_c)
-constexpr int kDH = 64;      // head-dim columns owned by one thread
+constexpr int kDH = 16;      // head-dim columns owned by one lane
+constexpr int kWavesF = 4;   // waves per workgroup
+constexpr int kThreadsF = 64 * kWavesF;
+
+template <int D>
+struct F32Lay {
+  static constexpr int TPR = D / kDH;    // lanes per query row
+  static constexpr int ROWS = kThreadsF / TPR;  // query rows per workgroup (B_r)
+};
+
+// Sum over the TPR lanes of a row (aligned groups of 4 or 8).
+template <int TPR>
+__device__ __forceinline__ float row_sum(float x) {
+  if constexpr (TPR == 8) return sum8(x);
+  x += dpp<0xB1>(x);
+  return x + dpp<0x4E>(x);
+}
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kRows * (D / kDH)) void fwd_f32_kernel(
+__global__ __launch_bounds__(kThreadsF) void fwd_f32_kernel(
     const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
     float* __restrict__ O, float* __restrict__ L, int Hq, int Hkv, int N, float c /* scale*log2e */) {
-  constexpr int TPR = D / kDH;  // threads per row
-  __shared__ float ks[kKeys][D];
-  __shared__ float vs[kKeys][D];
+  constexpr int TPR = F32Lay<D>::TPR;
+  constexpr int kRows = F32Lay<D>::ROWS;
+  __shared__ float4 ks[kKeys][D / 4];
+  __shared__ float4 vs[kKeys][D / 4];
 
   const int nqb = (N + kRows - 1) / kRows;
   const int bh = blockIdx.x / nqb;
@@ -37,12 +56,12 @@ __global__ __launch_bounds__(kRows * (D / kDH)) void fwd_f32_kernel(
   const int g = h / (Hq / Hkv);
   const int tid = threadIdx.x;
   const int row = qb * kRows + tid / TPR;
-  const int half = tid % TPR;
+  const int part = tid % TPR;  // this lane's 16 columns: part*16 .. part*16+15
   const bool row_ok = row < N;
 
-  const float* qp = Q + (((size_t)(b * Hq + h) * N) + (row_ok ? row : 0)) * D + half * kDH;
-  const float* kb = K + ((size_t)(b * Hkv + g) * N) * D;
-  const float* vb = V + ((size_t)(b * Hkv + g) * N) * D;
+  const float* qp = Q + (((size_t)(b * Hq + h) * N) + (row_ok ? row : 0)) * D + part * kDH;
+  const float4* kb = reinterpret_cast<const float4*>(K + ((size_t)(b * Hkv + g) * N) * D);
+  const float4* vb = reinterpret_cast<const float4*>(V + ((size_t)(b * Hkv + g) * N) * D);
 
   float q[kDH], o[kDH];
 #pragma unroll
@@ -55,11 +74,11 @@ __global__ __launch_bounds__(kRows * (D / kDH)) void fwd_f32_kernel(
   const int kend = CAUSAL ? min(N, (qb + 1) * kRows) : N;
   for (int j0 = 0; j0 < kend; j0 += kKeys) {
     __syncthreads();
-    for (int e = tid; e < kKeys * D; e += kRows * TPR) {
-      const int r = e / D, col = e % D;
+    for (int e = tid; e < kKeys * D / 4; e += kThreadsF) {
+      const int r = e / (D / 4), col = e % (D / 4);
       const bool ok = j0 + r < N;
-      ks[r][col] = ok ? kb[(size_t)(j0 + r) * D + col] : 0.f;
-      vs[r][col] = ok ? vb[(size_t)(j0 + r) * D + col] : 0.f;
+      ks[r][col] = ok ? kb[(size_t)(j0 + r) * (D / 4) + col] : make_float4(0.f, 0.f, 0.f, 0.f);
+      vs[r][col] = ok ? vb[(size_t)(j0 + r) * (D / 4) + col] : make_float4(0.f, 0.f, 0.f, 0.f);
     }
     __syncthreads();
     float s[kKeys];
@@ -68,8 +87,14 @@ __global__ __launch_bounds__(kRows * (D / kDH)) void fwd_f32_kernel(
     for (int j = 0; j < kKeys; ++j) {
       float acc = 0.f;
 #pragma unroll
-      for (int i = 0; i < kDH; ++i) acc = __builtin_fmaf(q[i], ks[j][half * kDH + i], acc);
-      if (TPR == 2) acc += dpp<0xB1>(acc);  // partner thread (l ^ 1) holds the other half
+      for (int i4 = 0; i4 < kDH / 4; ++i4) {
+        const float4 k4 = ks[j][part * (kDH / 4) + i4];
+        acc = __builtin_fmaf(q[4 * i4 + 0], k4.x, acc);
+        acc = __builtin_fmaf(q[4 * i4 + 1], k4.y, acc);
+        acc = __builtin_fmaf(q[4 * i4 + 2], k4.z, acc);
+        acc = __builtin_fmaf(q[4 * i4 + 3], k4.w, acc);
+      }
+      acc = row_sum<TPR>(acc);  // every lane of the row now holds the full dot product
       const int key = j0 + j;
       const bool vis = key < N && (!CAUSAL || key <= row);
       s[j] = vis ? acc : -INFINITY;
@@ -90,26 +115,32 @@ __global__ __launch_bounds__(kRows * (D / kDH)) void fwd_f32_kernel(
 #pragma unroll
     for (int j = 0; j < kKeys; ++j) {
 #pragma unroll
-      for (int i = 0; i < kDH; ++i) o[i] = __builtin_fmaf(s[j], vs[j][half * kDH + i], o[i]);
+      for (int i4 = 0; i4 < kDH / 4; ++i4) {
+        const float4 v4 = vs[j][part * (kDH / 4) + i4];
+        o[4 * i4 + 0] = __builtin_fmaf(s[j], v4.x, o[4 * i4 + 0]);
+        o[4 * i4 + 1] = __builtin_fmaf(s[j], v4.y, o[4 * i4 + 1]);
+        o[4 * i4 + 2] = __builtin_fmaf(s[j], v4.z, o[4 * i4 + 2]);
+        o[4 * i4 + 3] = __builtin_fmaf(s[j], v4.w, o[4 * i4 + 3]);
+      }
     }
     m = mnew;
   }
   if (!row_ok) return;
   const float inv = 1.f / l;
-  float* op = O + (((size_t)(b * Hq + h) * N) + row) * D + half * kDH;
+  float* op = O + (((size_t)(b * Hq + h) * N) + row) * D + part * kDH;
 #pragma unroll
   for (int i = 0; i < kDH; i += 4) {
     float4 w = make_float4(o[i] * inv, o[i + 1] * inv, o[i + 2] * inv, o[i + 3] * inv);
     *reinterpret_cast<float4*>(op + i) = w;
   }
-  if (half == 0) L[(size_t)(b * Hq + h) * N + row] = (m + log2_fast(l)) * kLn2;
+  if (part == 0) L[(size_t)(b * Hq + h) * N + row] = (m + log2_fast(l)) * kLn2;
 }
 
 template <int D, bool CAUSAL>
 hipError_t launch(const FwdArgs& a) {
-  const int nqb = (a.N + kRows - 1) / kRows;
+  const int nqb = (a.N + F32Lay<D>::ROWS - 1) / F32Lay<D>::ROWS;
   const dim3 grid((unsigned)(nqb * a.B * a.Hq));
-  const dim3 block(kRows * (D / kDH));
+  const dim3 block(kThreadsF);
   hipLaunchKernelGGL((fwd_f32_kernel<D, CAUSAL>), grid, block, 0, (hipStream_t)a.stream,
                      (const float*)a.q, (const float*)a.k, (const float*)a.v, (float*)a.o, a.lse,
                      a.Hq, a.Hkv, a.N, a.scale * kLog2e);
