@@ -76,6 +76,11 @@ SMALL = [
     (2, 2, 2, 65, 64, True, "f32"),
     (1, 1, 1, 1, 128, False, "f32"),
     (1, 3, 1, 200, 64, False, "f32"),
+    # fp32 rows split over 16-column lane slices: 32-row blocks at d = 128, 64 at d = 64,
+    # ragged against both, with grouped heads
+    (2, 4, 2, 333, 128, False, "f32"),
+    (1, 4, 1, 97, 64, True, "f32"),
+    (1, 2, 1, 161, 128, True, "f32"),
 ]
 
 
