@@ -433,12 +433,19 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void fwd_bf16_kernel(
   // The workgroups that read the same K/V (the G query heads of a group, and when
   // paged also the chunk's query blocks) are consecutive in that order.  Workgroups
   // are dealt to the 8 XCDs round-robin by linear index, so runs of S consecutive
-  // items are handed to one XCD (slot s of XCD x takes item (x + 8 (s / S)) S + s % S)
-  // and their K/V tiles are fetched from HBM once into that XCD's L2.  A ragged tail
-  // of fewer than 8 S items keeps the plain order.
+  // items are handed to one XCD and their K/V tiles are fetched from HBM once into
+  // that XCD's L2.  Runs go to the XCDs in snake order (round k of runs: XCD x takes
+  // run 8k + x, or 8k + 7 - x when k is odd): a run can be a whole causal query block
+  // (S = 32 with one K/V head), and dealing the heaviest runs to the same XCDs every
+  // round would leave the others idle at the end.  Slot s of XCD x takes item
+  // c S + s % S, with run c from round k = s / S.  A ragged tail of fewer than 8 S
+  // items keeps the plain order.
   const int S = PAGED ? G * nqb : G;
   int item = (int)blockIdx.x;
-  if (item < (int)(gridDim.x / (8 * S)) * 8 * S) item = ((item & 7) + 8 * ((item >> 3) / S)) * S + (item >> 3) % S;
+  if (item < (int)(gridDim.x / (8 * S)) * 8 * S) {
+    const int x = item & 7, slot = item >> 3, k = slot / S;
+    item = (8 * k + ((k & 1) ? 7 - x : x)) * S + slot % S;
+  }
   int qb, b, h;
   if constexpr (PAGED) {
     const int per_seq = Hkv * nqb * G;
