@@ -11,7 +11,12 @@ against the MI355X peaks (bf16 dense MFMA 2516.6 TFLOP/s = 256 CU x 2.4 GHz x 40
 flop/clk; HBM3E 8000 GB/s).  `cpu_baseline` times the fp64 CPU oracle on a bounded
 sample of the same workload.
 
-Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 30] [--no-cpu-baseline]
+Every timed measurement is warmed for at least --settle-ms of load first, the step
+included; the JSON line records the warm-up, per-step mean/median/min, the graphics
+clock sampled during the run, the software versions, and the errors of the timed
+step's outputs against the fp64 oracle (`numerics`).
+
+Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 200] [--no-cpu-baseline]
 """
 
 from __future__ import annotations
@@ -42,9 +47,10 @@ def log(msg):
 
 
 def warm(fn, n_min, ms_min=100.0):
-    """Untimed launches before a measurement beside the step: at least n_min, and at
-    least ms_min of wall time, since the GPU clock takes tens of milliseconds of load
-    to settle (a short kernel warmed by a few launches is timed at a lower clock)."""
+    """Untimed launches before a measurement: at least n_min, and at least ms_min of
+    wall time, since the GPU clock takes tens of milliseconds of load to settle (a
+    short kernel warmed by a few launches is timed at a lower clock).  Returns
+    (launches, milliseconds)."""
     import torch
 
     torch.cuda.synchronize()
@@ -56,6 +62,131 @@ def warm(fn, n_min, ms_min=100.0):
         if i % 8 == 0:
             torch.cuda.synchronize()
     torch.cuda.synchronize()
+    return i, (time.perf_counter() - t0) * 1e3
+
+
+class ClockSampler:
+    """The GPU's current graphics clock, sampled through amdsmi on a host thread while
+    launches run (a driver query; nothing is enqueued on the GPU).  Reports min, mean
+    and max MHz per phase, or why no reading was possible."""
+
+    def __init__(self, period_s=0.002):
+        import threading
+
+        self.period = period_s
+        self.samples = {}
+        self.phase = None
+        self.error = None
+        self._stop = threading.Event()
+        self._thread = None
+        self._read = None
+        try:
+            import amdsmi
+
+            amdsmi.amdsmi_init()
+            handles = amdsmi.amdsmi_get_processor_handles()
+            h = self._match(amdsmi, handles)
+            clk = amdsmi.AmdSmiClkType.GFX
+            self._read = lambda: float(amdsmi.amdsmi_get_clock_info(h, clk)["clk"])
+            self._read()
+        except Exception as e:  # no amdsmi, no permission, no device: report it, keep measuring
+            self.error = f"{type(e).__name__}: {e}"[:200]
+            self._read = None
+
+    @staticmethod
+    def _match(amdsmi, handles):
+        import torch
+
+        if not handles:
+            raise RuntimeError("amdsmi lists no GPU")
+        props = torch.cuda.get_device_properties(0)
+        bus = getattr(props, "pci_bus_id", None)
+        if bus is not None and len(handles) > 1:
+            for h in handles:
+                bdf = amdsmi.amdsmi_get_gpu_device_bdf(h)  # "dddd:bb:dd.f"
+                if int(bdf.split(":")[1], 16) == int(bus):
+                    return h
+        return handles[0]
+
+    def _run(self):
+        while not self._stop.is_set():
+            try:
+                v = self._read()
+                self.samples.setdefault(self.phase, []).append(v)
+            except Exception as e:
+                self.error = f"{type(e).__name__}: {e}"[:200]
+                return
+            time.sleep(self.period)
+
+    def start(self, phase):
+        import threading
+
+        self.phase = phase
+        if self._read is not None:
+            self._thread = threading.Thread(target=self._run, daemon=True)
+            self._thread.start()
+
+    def mark(self, phase):
+        self.phase = phase
+
+    def stop(self):
+        self._stop.set()
+        if self._thread is not None:
+            self._thread.join()
+        out = {"source": "amdsmi_get_clock_info(GFX) current clock, sampled every "
+                         f"{self.period * 1e3:.0f} ms on a host thread"}
+        for ph, v in self.samples.items():
+            out[ph] = {"min_mhz": min(v), "mean_mhz": round(sum(v) / len(v), 1), "max_mhz": max(v), "samples": len(v)}
+        if self.error:
+            out["error"] = self.error
+        return out
+
+
+def versions():
+    import torch
+
+    rocm = None
+    try:
+        with open("/opt/rocm/.info/version") as f:
+            rocm = f.read().strip()
+    except OSError:
+        pass
+    return {"torch": torch.__version__, "hip": torch.version.hip, "rocm": rocm, "python": sys.version.split()[0]}
+
+
+def host_cores():
+    return len(os.sched_getaffinity(0))
+
+
+def blas_threads():
+    import threadpoolctl
+
+    return max((i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()), default=1) or 1
+
+
+def output_check(O, L, Oref, Lref, tol_o=1e-2, tol_l=1e-3):
+    """Errors of the timed launch's outputs against the fp64 oracle (every compared
+    element): max-abs O and L, the bf16 output floor max|bf16(O_ref) - O_ref|, and the
+    number of O elements above the bar (allowed only where half a bf16 ulp of the exact
+    value exceeds the bar and the output is one of the two bf16 values around it)."""
+    import numpy as np
+    import torch
+
+    O = np.asarray(O, dtype=np.float64)
+    L = np.asarray(L, dtype=np.float64)
+    err = np.abs(O - Oref)
+    fin = np.isfinite(Lref)
+    rne = torch.from_numpy(np.ascontiguousarray(Oref)).to(torch.bfloat16).double().numpy()
+    over = err > tol_o
+    _, ex = np.frexp(Oref[over])
+    sp = np.ldexp(1.0, ex - 8)
+    lo = np.floor(Oref[over] / sp) * sp
+    faithful = (sp / 2 > tol_o) & ((O[over] == lo) | (O[over] == lo + sp))
+    el = float(np.abs(L[fin] - Lref[fin]).max()) if fin.any() else 0.0
+    return {"max_abs_O": float(err.max()), "max_abs_L": el, "bf16_floor": float(np.abs(rne - Oref).max()),
+            "tol_O": tol_o, "tol_L": tol_l, "elements": int(O.size), "above_tol_O": int(over.sum()),
+            "above_tol_O_faithful_bf16": int(faithful.sum()),
+            "pass": bool(np.all(np.isfinite(O)) and faithful.all() and el <= tol_l)}
 
 
 def source_digest(files):
@@ -104,32 +235,29 @@ def decode_bytes(x, cfg):
 
 
 def cpu_baseline_prefill(x, cfg, stride):
-    """fp64 oracle on every `stride`-th query row of every head (stride 1: the whole workload)."""
+    """fp64 oracle on every `stride`-th query row of every head (stride 1: the whole
+    workload).  Returns the baseline record, the rows and the oracle's O and L."""
     import numpy as np
-    import threadpoolctl
 
     from oracle import attention_ref
 
     q, k, v = (x[n].float().numpy() for n in "qkv")
     rows = np.arange(0, cfg.N, stride)
     t0 = time.perf_counter()
-    attention_ref(q, k, v, cfg.causal, cfg.scale, rows=rows)
+    Oref, Lref = attention_ref(q, k, v, cfg.causal, cfg.scale, rows=rows)
     dt = time.perf_counter() - t0
     vis = (rows + 1) if cfg.causal else np.full(rows.shape, cfg.N)
     flops = 4.0 * cfg.d * float(vis.sum()) * cfg.B * cfg.Hq
-    threads = max(i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()) or 1
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": (f"all {cfg.N} query rows" if stride == 1 else f"every {stride}th query row ({len(rows)} rows)")
-                      + f" of all {cfg.B * cfg.Hq} heads of {cfg.name}; "
-                      f"{dt:.1f} s of fp64 numpy",
-            "seconds": round(dt, 2)}
+    rec = {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": host_cores(), "threads": blas_threads(),
+           "kind": "oracle",
+           "sample": (f"all {cfg.N} query rows" if stride == 1 else f"every {stride}th query row ({len(rows)} rows)")
+                     + f" of all {cfg.B * cfg.Hq} heads of {cfg.name}; {dt:.1f} s of fp64 numpy",
+           "seconds": round(dt, 2)}
+    return rec, rows, Oref, Lref
 
 
 def cpu_baseline_backward(x, do, cfg, heads):
     """fp64 oracle gradients for the first `heads` query heads (and their K/V heads) of batch 0."""
-    import numpy as np
-    import threadpoolctl
-
     from oracle import attention_bwd_ref
 
     G = cfg.Hq // cfg.Hkv
@@ -142,17 +270,16 @@ def cpu_baseline_backward(x, do, cfg, heads):
     attention_bwd_ref(q, k, v, g, cfg.causal, cfg.scale)
     dt = time.perf_counter() - t0
     flops = 2.5 * 4.0 * heads * cfg.N * cfg.N * cfg.d / (2 if cfg.causal else 1)
-    threads = max(i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()) or 1
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": host_cores(), "threads": blas_threads(),
+            "kind": "oracle",
             "sample": f"{heads} of {cfg.B * cfg.Hq} query heads of {cfg.name} (every row and key); "
                       f"{dt:.1f} s of fp64 numpy",
             "seconds": round(dt, 2)}
 
 
 def cpu_baseline_decode(x, cfg, nseq):
-    import numpy as np
-    import threadpoolctl
-
+    """fp64 oracle on the first nseq sequences.  Returns the baseline record and the
+    oracle's O and L for those sequences."""
     from oracle import decode_ref
 
     kp = x["kpages"].float().numpy()  # bf16 -> fp32 view for numpy, outside the timed region
@@ -160,15 +287,16 @@ def cpu_baseline_decode(x, cfg, nseq):
     sub = slice(0, nseq)
     qs = x["q"][sub].float().numpy()
     t0 = time.perf_counter()
-    decode_ref(qs, kp, vp, x["page_table"][sub].numpy(), x["ctx_lens"][sub].numpy(), cfg.scale)
+    Oref, Lref = decode_ref(qs, kp, vp, x["page_table"][sub].numpy(), x["ctx_lens"][sub].numpy(), cfg.scale)
     dt = time.perf_counter() - t0
     ctx = x["ctx_lens"][sub].long()
     byts = int(ctx.sum()) * cfg.Hkv * cfg.d * 4 + 2 * nseq * cfg.Hq * cfg.d * 2
-    threads = max(i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()) or 1
-    return {"value": byts / dt / 1e9, "unit": "GB/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{nseq} of {cfg.num_seqs} sequences of {cfg.name} (all heads, every valid token); "
-                      f"{dt:.1f} s of fp64 numpy incl. the page gather",
-            "seconds": round(dt, 2)}
+    rec = {"value": byts / dt / 1e9, "unit": "GB/s", "cores": host_cores(), "threads": blas_threads(),
+           "kind": "oracle",
+           "sample": f"{nseq} of {cfg.num_seqs} sequences of {cfg.name} (all heads, every valid token); "
+                     f"{dt:.1f} s of fp64 numpy incl. the page gather",
+           "seconds": round(dt, 2)}
+    return rec, Oref, Lref
 
 
 def main():
@@ -178,6 +306,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=200,
                     help="untimed steps first (the GPU clock takes tens of milliseconds of load to settle; "
                          "200 steps are about 0.2 s)")
+    ap.add_argument("--settle-ms", type=float, default=300.0,
+                    help="warm-up floor in milliseconds of load before the timed steps (the clock settles "
+                         "within tens of milliseconds)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-row-stride", type=int, default=1,
                     help="oracle baseline on every n-th query row of the prefill (1 = the whole workload)")
@@ -258,17 +389,23 @@ def main():
     def decode():
         fa.fa_decode_paged(dq, kp, vp, pt, cl, scale=dcfg.scale, out=do, lse=dl, workspace=ws)
 
-    log(f"warmup {args.warmup}")
-    for _ in range(args.warmup):
+    def step():
         if run_p:
             prefill()
         if run_d:
             decode()
-    torch.cuda.synchronize()
+
+    # The step gets the same time-floored warm-up as every measurement beside it: at
+    # least --warmup steps and at least --settle-ms of load, so the clock has settled.
+    clocks = ClockSampler()
+    clocks.start("warmup")
+    n_warm, warm_ms = warm(step, args.warmup, ms_min=args.settle_ms)
+    log(f"warmup {n_warm} steps in {warm_ms:.0f} ms")
 
     K = args.steps
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
     log(f"timing {K} steps")
+    clocks.mark("timed")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K):
@@ -281,10 +418,19 @@ def main():
         ev[i][2].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    p_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / K
-    d_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / K
+    clock_rec = clocks.stop()
+    p_list = [e[0].elapsed_time(e[1]) for e in ev]
+    d_list = [e[1].elapsed_time(e[2]) for e in ev]
+    p_ms = sum(p_list) / K
+    d_ms = sum(d_list) / K
     step_ms = ev[0][0].elapsed_time(ev[-1][2]) / K
     log(f"prefill {p_ms:.4f} ms, decode {d_ms:.4f} ms, step {step_ms:.4f} ms (wall {wall * 1e3 / K:.4f} ms)")
+
+    def stats(v):
+        import statistics
+
+        return {"mean_ms": round(sum(v) / len(v), 5), "median_ms": round(statistics.median(v), 5),
+                "min_ms": round(min(v), 5), "max_ms": round(max(v), 5)}
 
     bwd = None
     if run_b or run_w:
@@ -305,7 +451,7 @@ def main():
             fa.fa_bwd(bq, bk, bv, bo, bl, bdo, causal=pcfg.causal, scale=pcfg.scale, dq=bdq, dk=bdk, dv=bdv,
                       workspace=bws)
 
-        warm(backward, max(1, args.warmup // 3))
+        warm(backward, max(1, args.warmup // 3), ms_min=args.settle_ms)
         bev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
         for i in range(K):
             bev[i][0].record()
@@ -336,7 +482,7 @@ def main():
         def windowed():
             fa.fa_fwd_ex(bq, bk, bv, causal=True, scale=pcfg.scale, window=W, alibi_slopes=slopes, out=wo, lse=wl)
 
-        warm(windowed, max(1, args.warmup // 3))
+        warm(windowed, max(1, args.warmup // 3), ms_min=args.settle_ms)
         wev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
         for i in range(K):
             wev[i][0].record()
@@ -371,7 +517,7 @@ def main():
             fa.fa_prefill_paged(cg["q"], cg["kpages"], cg["vpages"], cg["page_table"], cg["ctx_lens"], out=co,
                                 lse=cl)
 
-        warm(chunked, max(1, args.warmup // 3))
+        warm(chunked, max(1, args.warmup // 3), ms_min=args.settle_ms)
         cev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
         for i in range(K):
             cev[i][0].record()
@@ -408,7 +554,7 @@ def main():
             fa.fa_decode_paged_int8(ig["q"], ig["kq"], ig["kscale"], ig["vq"], ig["vscale"], ig["page_table"],
                                     ig["ctx_lens"], out=io, lse=il, workspace=iws)
 
-        warm(int8_decode, max(1, args.warmup // 3))
+        warm(int8_decode, max(1, args.warmup // 3), ms_min=args.settle_ms)
         iev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
         for i in range(K):
             iev[i][0].record()
@@ -446,7 +592,7 @@ def main():
             def other():
                 fwd(oq, ok_, ov, causal=ocfg.causal, scale=ocfg.scale, out=oo, lse=ol)
 
-            warm(other, max(1, args.warmup // 3))
+            warm(other, max(1, args.warmup // 3), ms_min=args.settle_ms)
             oev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
             for i in range(K):
                 oev[i][0].record()
@@ -466,7 +612,14 @@ def main():
 
     res = {"metric": METRIC, "n_gpus": 1, "steps": K, "warmup": args.warmup, "ms_per_step": round(step_ms, 5),
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
-           "data": "synthetic (seeded N(0,1) inputs; random page permutation)"}
+           "data": "synthetic (seeded N(0,1) inputs; random page permutation)",
+           "timing": {"warmup_steps": n_warm, "warmup_ms": round(warm_ms, 1),
+                      "settle_floor_ms": args.settle_ms, "events": "HIP events on the launch stream"},
+           "sclk": clock_rec, "versions": versions()}
+    if run_p:
+        res["timing"]["prefill"] = stats(p_list)
+    if run_d:
+        res["timing"]["decode"] = stats(d_list)
     cfg_desc = {"workload": "one step = causal bf16 prefill B1 Hq32 Hkv32 N8192 d128 (inputs 0.5*N(0,1)) "
                             "+ paged bf16 decode 64 seqs Hq32 Hkv8 d128 ctx~U[1024,16384] 16-token pages"}
     if run_p:
@@ -512,15 +665,30 @@ def main():
             res.update({"value": None, "unit": "TFLOP/s", "roofline": None})
     res["config"] = cfg_desc
     if not args.no_cpu_baseline:
+        # the oracle's results also check the outputs of the last timed step
         log("timing the fp64 CPU oracle on a bounded sample")
+        numerics = {}
         if run_p:
-            res["cpu_baseline"] = cpu_baseline_prefill(px, pcfg, args.cpu_row_stride)
+            cb, rows, Oref, Lref = cpu_baseline_prefill(px, pcfg, args.cpu_row_stride)
+            res["cpu_baseline"] = cb
+            ri = torch.from_numpy(rows).to(dev)
+            numerics[PREFILL] = output_check(o[:, :, ri].double().cpu().numpy(), lse[:, :, ri].double().cpu().numpy(),
+                                             Oref, Lref)
+            numerics[PREFILL]["rows"] = "all" if args.cpu_row_stride == 1 else f"every {args.cpu_row_stride}th"
+            del Oref, Lref
         if run_d:
-            cb = cpu_baseline_decode(dx, dcfg, min(args.cpu_decode_seqs, dcfg.num_seqs))
+            nseq = min(args.cpu_decode_seqs, dcfg.num_seqs)
+            cb, Oref, Lref = cpu_baseline_decode(dx, dcfg, nseq)
+            numerics[DECODE] = output_check(do[:nseq].double().cpu().numpy(), dl[:nseq].double().cpu().numpy(),
+                                            Oref, Lref)
+            numerics[DECODE]["sequences"] = nseq
             if run_p:
                 res["decode"]["cpu_baseline"] = cb
             else:
                 res["cpu_baseline"] = cb
+        res["numerics"] = numerics
+        log("numerics: " + ", ".join(f"{k} max|dO| {v['max_abs_O']:.2e} max|dL| {v['max_abs_L']:.2e} "
+                                     f"floor {v['bf16_floor']:.2e} pass {v['pass']}" for k, v in numerics.items()))
         if bwd is not None:
             bcb = cpu_baseline_backward(bx, bdo_cpu, pcfg, args.cpu_bwd_heads)
             if "cpu_baseline" in res:

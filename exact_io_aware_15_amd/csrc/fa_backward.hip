@@ -48,6 +48,9 @@ constexpr int kWaveRows = 32;                // query rows (dQ) or keys (dK/dV) 
 constexpr int kBlockRows = kBwdWaves * kWaveRows;  // 128 keys per dK/dV workgroup
 constexpr int kDqRows = kDqWaves * kWaveRows;      // 256 query rows per dQ workgroup
 constexpr int kTile = 64;                    // rows of the streamed operand per tile
+static_assert(kDqRows == kGeomDqRows && kDqWaves * 64 == kGeomDqThreads && kBlockRows == kGeomDkdvRows &&
+                  kBwdThreads == kGeomDkdvThreads,
+              "host-side launch limits assume this geometry");
 
 template <int D, int W = kBwdWaves>
 struct BLay {

@@ -37,6 +37,7 @@ typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 constexpr int kPage = 16;
 constexpr int kDecWaves = 4;
 constexpr int kDecThreads = kDecWaves * 64;
+static_assert(kDecThreads == kGeomDecThreads, "host-side launch limits assume this workgroup size");
 
 __device__ __forceinline__ u32x4 ldg16(const uint16_t* p) { return *reinterpret_cast<const u32x4*>(p); }
 // Cache pages are read exactly once per call: the loads carry the non-temporal hint
@@ -50,7 +51,7 @@ template <int D, int HB>
 __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ KPg, const uint16_t* __restrict__ VPg,
     const int32_t* __restrict__ table, const int32_t* __restrict__ ctx, float* __restrict__ ws_o,
-    float* __restrict__ ws_l, int Hq, int Hkv, int max_pages, int max_splits, int nhb, float c) {
+    float* __restrict__ ws_l, int Hq, int Hkv, int max_pages, int num_pages, int max_splits, int nhb, float c) {
   constexpr int CPL = D / 64;  // 8-column chunks per token per lane
   constexpr int DL = CPL * 8;  // d columns per lane
   constexpr int PP = 2;        // pages consumed per wave iteration
@@ -64,7 +65,10 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
   const int g = (blockIdx.x / nhb) % Hkv;
   const int s = blockIdx.x / (nhb * Hkv);
   const int G = Hq / Hkv;
-  const int n = ctx[s];
+  // device-side sizes are clamped to the buffers the host described: the context to
+  // the page table's row, page ids to the pools (out-of-range values give wrong
+  // output, never an access outside the buffers)
+  const int n = min(max(ctx[s], 0), max_pages * kPage);
   const int npages = (n + kPage - 1) / kPage;
   const int p_begin = split * kDecodePagesPerSplit;
   if (p_begin >= npages) return;  // this split has no tokens: nothing is written or read later
@@ -117,7 +121,8 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
 #pragma unroll
   for (int r = 0; r < kIdRegs; ++r) {
     const int pg = p_begin + 64 * r + (tid & 63);
-    lane_pid[r] = pg < p_end ? trow[pg] : 0;
+    const int id = pg < p_end ? trow[pg] : 0;
+    lane_pid[r] = (unsigned)id < (unsigned)num_pages ? id : num_pages - 1;
   }
   auto page_id = [&](int idx) {  // idx wave-uniform, 0 <= idx < kDecodePagesPerSplit
     int id = __builtin_amdgcn_readlane(lane_pid[0], idx & 63);
@@ -333,7 +338,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_int8_kernel(
     const uint16_t* __restrict__ Q, const int8_t* __restrict__ KQ, const float* __restrict__ KS,
     const int8_t* __restrict__ VQ, const float* __restrict__ VS, const int32_t* __restrict__ table,
     const int32_t* __restrict__ ctx, float* __restrict__ ws_o, float* __restrict__ ws_l, int Hq, int Hkv,
-    int max_pages, int max_splits, int nhb, float c) {
+    int max_pages, int num_pages, int max_splits, int nhb, float c) {
   constexpr int CH = D / 8;           // channels per lane
   constexpr int NG = D / 32;          // scale groups per token
   constexpr int NW = CH / 4;          // 32-bit words per token per lane
@@ -349,7 +354,10 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_int8_kernel(
   const int g = (blockIdx.x / nhb) % Hkv;
   const int s = blockIdx.x / (nhb * Hkv);
   const int G = Hq / Hkv;
-  const int n = ctx[s];
+  // device-side sizes are clamped to the buffers the host described: the context to
+  // the page table's row, page ids to the pools (out-of-range values give wrong
+  // output, never an access outside the buffers)
+  const int n = min(max(ctx[s], 0), max_pages * kPage);
   const int npages = (n + kPage - 1) / kPage;
   const int p_begin = split * kDecodePagesPerSplit;
   if (p_begin >= npages) return;
@@ -421,7 +429,8 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_int8_kernel(
 #pragma unroll
   for (int r = 0; r < kIdRegs; ++r) {
     const int pg = p_begin + 64 * r + (tid & 63);
-    lane_pid[r] = pg < p_end ? trow[pg] : 0;
+    const int id = pg < p_end ? trow[pg] : 0;
+    lane_pid[r] = (unsigned)id < (unsigned)num_pages ? id : num_pages - 1;
   }
   auto page_id = [&](int idx) {
     int id = __builtin_amdgcn_readlane(lane_pid[0], idx & 63);
@@ -595,11 +604,11 @@ __global__ __launch_bounds__(D) void decode_merge_kernel(const float* __restrict
                                                          const float* __restrict__ ws_l,
                                                          const int32_t* __restrict__ ctx,
                                                          uint16_t* __restrict__ O, float* __restrict__ Lse,
-                                                         int Hq, int max_splits) {
+                                                         int Hq, int max_pages, int max_splits) {
   const int s = blockIdx.x / Hq;
   const int h = blockIdx.x % Hq;
   const int d = threadIdx.x;
-  const int n = ctx[s];
+  const int n = min(ctx[s], max_pages * kPage);  // as in the split kernels
   const size_t out = ((size_t)s * Hq + h);
   if (n <= 0) {
     O[out * D + d] = 0;
@@ -628,7 +637,7 @@ hipError_t launch_split(const DecodeArgs& a, float* ws_o, float* ws_l, int max_s
   const dim3 grid((unsigned)(a.S * a.Hkv * nhb), (unsigned)max_splits);
   hipLaunchKernelGGL((decode_split_kernel<D, HB>), grid, dim3(kDecThreads), 0, (hipStream_t)a.stream,
                      (const uint16_t*)a.q, (const uint16_t*)a.kpages, (const uint16_t*)a.vpages, a.page_table,
-                     a.ctx_lens, ws_o, ws_l, a.Hq, a.Hkv, a.max_pages, max_splits, nhb, a.scale * kLog2e);
+                     a.ctx_lens, ws_o, ws_l, a.Hq, a.Hkv, a.max_pages, a.num_pages, max_splits, nhb, a.scale * kLog2e);
   return hipGetLastError();
 }
 
@@ -639,8 +648,8 @@ hipError_t launch_split_int8(const DecodeArgs& a, float* ws_o, float* ws_l, int 
   const dim3 grid((unsigned)(a.S * a.Hkv * nhb), (unsigned)max_splits);
   hipLaunchKernelGGL((decode_split_int8_kernel<D, HB>), grid, dim3(kDecThreads), 0, (hipStream_t)a.stream,
                      (const uint16_t*)a.q, (const int8_t*)a.kpages, a.kscale, (const int8_t*)a.vpages, a.vscale,
-                     a.page_table, a.ctx_lens, ws_o, ws_l, a.Hq, a.Hkv, a.max_pages, max_splits, nhb,
-                     a.scale * kLog2e);
+                     a.page_table, a.ctx_lens, ws_o, ws_l, a.Hq, a.Hkv, a.max_pages, a.num_pages, max_splits,
+                     nhb, a.scale * kLog2e);
   return hipGetLastError();
 }
 
@@ -661,7 +670,7 @@ hipError_t launch_d(const DecodeArgs& a) {
   else e = launch_split<D, 4>(a, ws_o, ws_l, max_splits);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((decode_merge_kernel<D>), dim3((unsigned)(a.S * a.Hq)), dim3(D), 0, (hipStream_t)a.stream,
-                     ws_o, ws_l, a.ctx_lens, (uint16_t*)a.o, a.lse, a.Hq, max_splits);
+                     ws_o, ws_l, a.ctx_lens, (uint16_t*)a.o, a.lse, a.Hq, a.max_pages, max_splits);
   return hipGetLastError();
 }
 

@@ -25,6 +25,7 @@ struct FwdArgs {
   const int32_t* page_table = nullptr;
   const int32_t* ctx_lens = nullptr;
   int max_pages = 0;
+  int num_pages = 0;              // pages in each pool (page ids are clamped below it)
 };
 
 struct DecodeArgs {
@@ -35,7 +36,7 @@ struct DecodeArgs {
   const int32_t* ctx_lens;
   void* o;
   float* lse;
-  int S, Hq, Hkv, d, page_size, max_pages;
+  int S, Hq, Hkv, d, page_size, max_pages, num_pages;
   float scale;
   void* workspace;
   void* stream;
@@ -44,6 +45,19 @@ struct DecodeArgs {
   const float* kscale = nullptr;
   const float* vscale = nullptr;
 };
+
+// Workgroup geometry of the kernels, shared with the host-side validation: a
+// dispatch's total work-item count (workgroups x threads) must stay below 2^31.
+// Each kernel source checks its own constants against these.
+constexpr int kGeomFwdRows = 256;     // bf16 forward: query rows per workgroup
+constexpr int kGeomFwdThreads = 512;
+constexpr int kGeomF32Threads = 256;  // fp32 forward: d / 16 lanes per row, so 256 / (d / 16) rows
+constexpr int kGeomDecThreads = 256;  // decode split kernel (the merge kernel has d threads)
+constexpr int kGeomDqRows = 256;      // backward dQ: query rows per workgroup
+constexpr int kGeomDqThreads = 512;
+constexpr int kGeomDkdvRows = 128;    // backward dK/dV: keys per workgroup
+constexpr int kGeomDkdvThreads = 512;
+constexpr long long kMaxWorkItems = 0x7fffffffLL;
 
 // Pages handled by one split of the paged decode.  The workspace size depends on it.
 #ifndef FA_DECODE_PAGES_PER_SPLIT

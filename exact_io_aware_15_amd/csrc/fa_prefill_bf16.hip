@@ -52,6 +52,7 @@ constexpr int kRowsPerWave = 32;            // one 32-row MFMA block per wave
 constexpr int kWaves = FA_PREFILL_WAVES;    // waves per workgroup (8: two per SIMD)
 constexpr int kThreads = kWaves * 64;
 constexpr int kBR = kWaves * kRowsPerWave;  // 256 query rows per workgroup
+static_assert(kBR == kGeomFwdRows && kThreads == kGeomFwdThreads, "host-side launch limits assume this geometry");
 constexpr float kRescaleThreshold = 8.0f;   // log2 units: probabilities stay <= 256
 constexpr int kPrefetch = 4;                // LDS fragment reads kept ahead of the MFMAs
 #ifndef FA_PREFILL_STAGES
@@ -384,8 +385,8 @@ __device__ __forceinline__ void copy_tile(uint8_t* smem, const void* kbase, cons
 // whole pages past it, whose table entries are never read -- land as zeros.
 template <int D>
 __device__ __forceinline__ void copy_tile_paged(uint8_t* smem, const uint16_t* kpool, const uint16_t* vpool,
-                                                const int32_t* trow, int nk, int Hkv, int g, int j0, int buf, int w,
-                                                int lane) {
+                                                const int32_t* trow, int nk, int num_pages, int Hkv, int g, int j0,
+                                                int buf, int w, int lane) {
   using LY = Lay<D>;
   uint8_t* kb = smem + buf * LY::TBYTES;
   uint8_t* vb = smem + (kStages + buf) * LY::TBYTES;
@@ -398,7 +399,8 @@ __device__ __forceinline__ void copy_tile_paged(uint8_t* smem, const uint16_t* k
     // descriptors are too (a vector clamp here made the compiler wrap every copy in
     // a loop over distinct descriptor values)
     const int valid = __builtin_amdgcn_readfirstlane(min(max(nk - tp * 16, 0), 16));
-    const int pid = valid > 0 ? trow[tp] : 0;
+    const int id = valid > 0 ? trow[tp] : 0;
+    const int pid = (unsigned)id < (unsigned)num_pages ? id : num_pages - 1;  // ids stay inside the pools
     const size_t head = ((size_t)pid * Hkv + g) * 16 * D;
     const auto krs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(kpool + head), (short)0,
                                                        (uint32_t)valid * LY::ROWB, 0x00020000);
@@ -420,7 +422,7 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void fwd_bf16_kernel(
     float c /* |scale| * log2(e), > 0 */, uint32_t qsign /* 0x80008000 if scale < 0 */,
     int window /* EXT: keys j >= i - window + 1 only (0: none) */, const float* __restrict__ slopes /* EXT: ALiBi */,
     const int32_t* __restrict__ table /* PAGED */, const int32_t* __restrict__ ctxl /* PAGED */,
-    int max_pages /* PAGED */) {
+    int max_pages /* PAGED */, int num_pages /* PAGED */) {
   using LY = Lay<D>;
   constexpr int KK = D / 16;
   constexpr int DB = D / 32;
@@ -478,7 +480,9 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void fwd_bf16_kernel(
   const uint16_t* kbase = K + (PAGED ? 0 : ((size_t)(b * Hkv + g) * N) * D);
   const uint16_t* vbase = V + (PAGED ? 0 : ((size_t)(b * Hkv + g) * N) * D);
   // keys and the position of query row 0 (the chunk's first token when paged)
-  const int Nk = PAGED ? ctxl[b] : N;
+  // (paged: the context is clamped to [chunk, page-table row], so a wrong device-side
+  // value gives wrong output but every access stays inside the buffers)
+  const int Nk = PAGED ? min(max(ctxl[b], N), max_pages * 16) : N;
   const int poff = PAGED ? Nk - N : 0;
   const int rw0p = rw0 + poff;
   const int qrowp = qrow + poff;
@@ -576,7 +580,7 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void fwd_bf16_kernel(
   for (int p = 0; p < kStages - 1; ++p)
     if (t_begin + p < ntiles) {
       if constexpr (PAGED)
-        copy_tile_paged<D>(smem, K, V, trow, Nk, Hkv, g, (rev ? ntiles - 1 - p : t_begin + p) * LY::BC, p, w, lane);
+        copy_tile_paged<D>(smem, K, V, trow, Nk, num_pages, Hkv, g, (rev ? ntiles - 1 - p : t_begin + p) * LY::BC, p, w, lane);
       else
         copy_tile<D>(smem, kbase, vbase, head_bytes, kcp, vcp, (rev ? ntiles - 1 - p : t_begin + p) * LY::BC, p, w);
     }
@@ -593,7 +597,7 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void fwd_bf16_kernel(
       const int j0 = rev ? (ntiles - 1 - (t - t_begin)) * LY::BC : t * LY::BC;
       if (t + kStages - 1 < ntiles) {
         if constexpr (PAGED)
-          copy_tile_paged<D>(smem, K, V, trow, Nk, Hkv, g, rev ? j0 - kAhead : j0 + kAhead, (u + kStages - 1) % kStages, w,
+          copy_tile_paged<D>(smem, K, V, trow, Nk, num_pages, Hkv, g, rev ? j0 - kAhead : j0 + kAhead, (u + kStages - 1) % kStages, w,
                              lane);
         else
           copy_tile<D>(smem, kbase, vbase, head_bytes, kcp, vcp, rev ? j0 - kAhead : j0 + kAhead,
@@ -669,7 +673,7 @@ hipError_t launch(const FwdArgs& a) {
   hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, EXT, PAGED>), grid, dim3(kThreads), 0, (hipStream_t)a.stream,
                      (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o,
                      a.lse, a.B, a.Hq, a.Hkv, a.N, c, qsign, a.window, a.slopes, a.page_table, a.ctx_lens,
-                     a.max_pages);
+                     a.max_pages, a.num_pages);
   return hipGetLastError();
 }
 

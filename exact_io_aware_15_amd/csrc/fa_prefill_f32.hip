@@ -24,6 +24,7 @@ constexpr int kKeys = 64;    // keys per tile (B_c)
 constexpr int kDH = 16;      // head-dim columns owned by one lane
 constexpr int kWavesF = 4;   // waves per workgroup
 constexpr int kThreadsF = 64 * kWavesF;
+static_assert(kThreadsF == kGeomF32Threads, "host-side launch limits assume this workgroup size");
 
 template <int D>
 struct F32Lay {

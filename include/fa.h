@@ -26,8 +26,14 @@
  *     makes every call synchronise the stream and report kernel errors.
  *   - Arguments are validated on the host before any HIP call; a failed check
  *     returns its status code and launches nothing.
- *   - A zero batch (B == 0, N == 0, or num_seqs == 0) is a no-op returning
- *     FA_OK; pointers may then be NULL.
+ *   - Every size is at least 1: B, Hq, Hkv, N, num_seqs, chunk, max_pages_per_seq
+ *     and num_pages below 1 return FA_ERR_SHAPE.  So do sizes past the kernels'
+ *     limits: a launch must stay below 2^31 work-items, and the bf16 kernels
+ *     address one (batch, head) slice of N x d values through a 32-bit byte
+ *     range, so N * d * 2 must not exceed 2^32 - 1 (N < 2^24 at d = 128).
+ *   - Validation order: sizes (FA_ERR_SHAPE), head dimension / page size
+ *     (FA_ERR_UNSUPPORTED), scale (FA_ERR_SCALE), pointers (FA_ERR_NULL, then
+ *     FA_ERR_ALIGN), workspace (FA_ERR_WORKSPACE).
  *   - Thread safety: the library has no mutable global state besides a
  *     thread-local copy of the last HIP error text.
  */
@@ -44,7 +50,7 @@ extern "C" {
 /* Status codes. */
 #define FA_OK              0 /* enqueued (or nothing to do)                        */
 #define FA_ERR_NULL        1 /* a required pointer is NULL                         */
-#define FA_ERR_SHAPE       2 /* negative size, Hq % Hkv != 0, Hq or Hkv < 1, ...   */
+#define FA_ERR_SHAPE       2 /* a size < 1, Hq % Hkv != 0, or past a kernel limit */
 #define FA_ERR_UNSUPPORTED 3 /* head dim not 64/128, page_size not 16             */
 #define FA_ERR_SCALE       4 /* scale is NaN or infinite                           */
 #define FA_ERR_ALIGN       5 /* a tensor pointer is not 16-byte aligned            */
@@ -65,8 +71,8 @@ extern "C" {
  *   q   [B, Hq,  N, d] bf16      k, v [B, Hkv, N, d] bf16
  *   o   [B, Hq,  N, d] bf16 (out, fp32 accumulation, rounded to nearest even)
  *   lse [B, Hq,  N]    fp32 (out, natural-log logsumexp of the scaled scores)
- *   d in {64, 128}; Hq % Hkv == 0; N >= 0; causal: 0 or 1 (query i sees keys
- *   j <= i); scale: any finite float (usually 1/sqrt(d)).
+ *   d in {64, 128}; Hq % Hkv == 0; B, N >= 1 and N * d * 2 < 2^32; causal: 0 or
+ *   1 (query i sees keys j <= i); scale: any finite float (usually 1/sqrt(d)).
  * Returns FA_OK or a status code above.
  */
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
@@ -116,10 +122,14 @@ int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
  *   lse        [S, Hq, chunk] fp32 (out, natural-log logsumexp)
  *   kpages, vpages, page_table, num_pages, max_pages_per_seq: as fa_decode_paged.
  *   ctx_lens   [S] int32, chunk <= ctx_lens[s] <= max_pages_per_seq * page_size
- *              (device data, trusted).  Cache slots at or beyond ctx_lens[s] never
- *              affect the result, whatever they hold.
- *   d in {64, 128}; page_size == 16; Hq % Hkv == 0; any finite scale.  No
- *   workspace.  S = 0 or chunk = 0 is a no-op.
+ *              (device data).  Cache slots at or beyond ctx_lens[s] never affect
+ *              the result, whatever they hold.  A value outside that range, or a
+ *              page id outside [0, num_pages), gives wrong output but no access
+ *              outside the buffers: the kernel clamps ctx_lens[s] into
+ *              [chunk, max_pages_per_seq * page_size] and page ids into
+ *              [0, num_pages - 1].
+ *   d in {64, 128}; page_size == 16; Hq % Hkv == 0; 1 <= chunk <=
+ *   max_pages_per_seq * page_size; any finite scale.  No workspace.
  */
 int fa_prefill_paged(const void* q, const void* kpages, const void* vpages,
                      const int32_t* page_table, const int32_t* ctx_lens,
@@ -155,7 +165,8 @@ size_t fa_bwd_workspace_size(int B, int Hq, int Hkv, int N, int d);
  *   workspace: device memory of at least fa_bwd_workspace_size(B, Hq, Hkv, N, d)
  *   bytes, 16-byte aligned, owned by the caller; contents on entry do not matter.
  *   Calls sharing a workspace must be ordered (same stream).
- *   d in {64, 128}; Hq % Hkv == 0; N >= 0; causal 0 or 1; any finite scale.
+ *   d in {64, 128}; Hq % Hkv == 0; B, N >= 1, N * d * 2 < 2^32; causal 0 or 1;
+ *   any finite scale.
  * Returns FA_OK or a status code above (FA_ERR_WORKSPACE for a missing or short
  * workspace).
  */
@@ -199,8 +210,10 @@ size_t fa_decode_paged_workspace_size(int num_seqs, int Hq, int d,
  *   page_size) bytes, owned by the caller, 16-byte aligned; its contents on
  *   entry do not matter.  Two calls that share a workspace must be ordered
  *   (same stream).
- * Device-side values (ctx_lens, page ids) are trusted: out-of-range values give
- * undefined output.  num_pages is used only by FA_DEBUG checks.
+ * num_pages: physical pages in each pool (>= 1).  Device-side values out of
+ * range give wrong output but no access outside the buffers: the kernels clamp
+ * ctx_lens[s] into [0, max_pages_per_seq * page_size] and page ids into
+ * [0, num_pages - 1].
  */
 int fa_decode_paged(const void* q, const void* kpages, const void* vpages,
                     const int32_t* page_table, const int32_t* ctx_lens,

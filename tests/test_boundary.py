@@ -67,9 +67,18 @@ def test_fwd_validation(L, entry):
     assert fwd(L, entry, scale=float("inf")) == SCALE
     assert fwd(L, entry, k=MIS) == ALIGN
     assert fwd(L, entry, o=MIS) == ALIGN
-    # empty inputs are a no-op that needs no pointers
-    assert fwd(L, entry, q=Z, k=Z, v=Z, o=Z, lse=Z, B=0) == OK
-    assert fwd(L, entry, q=Z, k=Z, v=Z, o=Z, lse=Z, N=0) == OK
+    # every size is at least 1: an empty batch or sequence is a shape error
+    assert fwd(L, entry, B=0) == SHAPE
+    assert fwd(L, entry, N=0) == SHAPE
+    assert fwd(L, entry, Hq=0) == SHAPE
+    # dispatch limits: fewer than 2^31 work-items per launch
+    rows = {"fa_fwd": 256, "fa_fwd_f32": 256 // 4}[entry]
+    threads = {"fa_fwd": 512, "fa_fwd_f32": 256}[entry]
+    blocks_max = (2**31 - 1) // threads
+    assert fwd(L, entry, B=blocks_max // 2 + 1, Hq=2, Hkv=1, N=rows) == SHAPE
+    # (the same sizes one workgroup fewer pass the size checks and stop at the NULL pointer;
+    # no call here may reach a launch)
+    assert fwd(L, entry, B=blocks_max // 2, Hq=2, Hkv=1, N=rows, q=Z) == NULL
 
 
 def dec(L, q=P, kp=P, vp=P, pt=P, cl=P, o=P, lse=P, S=2, Hq=8, Hkv=2, d=128, ps=16, maxp=4, npages=9,
@@ -93,7 +102,11 @@ def test_decode_validation(L):
     need = fa.fa_decode_paged_workspace_size(2, 8, 128, 4, 16)
     assert dec(L, wsb=need - 1) == WORKSPACE
     assert dec(L, ws=MIS, wsb=need) == ALIGN
-    assert dec(L, q=Z, kp=Z, vp=Z, pt=Z, cl=Z, o=Z, lse=Z, ws=Z, S=0) == OK
+    assert dec(L, S=0) == SHAPE
+    assert dec(L, Hq=0) == SHAPE
+    assert dec(L, npages=0) == SHAPE
+    # split grid: num_seqs * Hq * splits workgroups of 256 threads below 2^31 work-items
+    assert dec(L, S=(2**31 - 1) // 256 // 8 + 1, Hq=8, Hkv=2, maxp=4, wsb=1 << 62) == SHAPE
 
 
 def test_workspace_size(L):
@@ -125,7 +138,11 @@ def test_bwd_validation(L):
     need = fa.fa_bwd_workspace_size(1, 2, 1, 16, 64)
     assert bwd(L, wsb=need - 1) == WORKSPACE
     assert bwd(L, ws=MIS, wsb=need) == ALIGN
-    assert bwd(L, q=Z, k=Z, v=Z, o=Z, lse=Z, do=Z, dq=Z, dk=Z, dv=Z, ws=Z, B=0) == OK
+    assert bwd(L, B=0) == SHAPE
+    assert bwd(L, N=0) == SHAPE
+    # the bf16 kernels address one (batch, head) slice through a 32-bit byte range
+    assert bwd(L, N=2**24, d=128, B=1, Hq=1, Hkv=1) == SHAPE          # 2^24 * 128 * 2 = 4 GiB
+    assert bwd(L, N=2**24 - 64, d=128, B=1, Hq=1, Hkv=1, q=Z) == NULL
 
 
 def test_bwd_workspace_size(L):
@@ -154,7 +171,11 @@ def test_fwd_ex_validation(L):
     assert fwd_ex(L, slopes=ctypes.c_void_p(0x10002)) == ALIGN
     assert fwd_ex(L, q=Z) == NULL
     assert fwd_ex(L, d=80) == UNSUP
-    assert fwd_ex(L, window=3, q=Z, k=Z, v=Z, o=Z, lse=Z, N=0) == OK
+    assert fwd_ex(L, window=3, N=0) == SHAPE
+    assert fwd_ex(L, B=0) == SHAPE
+    assert fwd_ex(L, N=2**24, d=128, B=1, Hq=1, Hkv=1) == SHAPE
+    assert fwd_ex(L, N=2**25, d=64, B=1, Hq=1, Hkv=1) == SHAPE
+    assert fwd_ex(L, N=2**25 - 64, d=64, B=1, Hq=1, Hkv=1, q=Z) == NULL
 
 
 def pp(L, q=P, kp=P, vp=P, pt=P, cl=P, o=P, lse=P, S=2, Hq=8, Hkv=2, d=128, C=5, ps=16, maxp=4, npages=9,
@@ -170,8 +191,12 @@ def test_prefill_paged_validation(L):
     assert pp(L, C=-1) == SHAPE
     assert pp(L, scale=float("nan")) == SCALE
     assert pp(L, o=MIS) == ALIGN
-    assert pp(L, q=Z, kp=Z, vp=Z, pt=Z, cl=Z, o=Z, lse=Z, C=0) == OK
-    assert pp(L, q=Z, kp=Z, vp=Z, pt=Z, cl=Z, o=Z, lse=Z, S=0) == OK
+    assert pp(L, C=0) == SHAPE
+    assert pp(L, S=0) == SHAPE
+    assert pp(L, npages=0) == SHAPE
+    # a chunk lies inside its sequence's cache: at most max_pages_per_seq * 16 tokens
+    assert pp(L, C=4 * 16 + 1, maxp=4) == SHAPE
+    assert pp(L, C=4 * 16, maxp=4, q=Z) == NULL
 
 
 def d8(L, q=P, kq=P, ks=P, vq=P, vs=P, pt=P, cl=P, o=P, lse=P, S=2, Hq=8, Hkv=2, d=128, ps=16, group=32, maxp=4,
@@ -188,4 +213,19 @@ def test_decode_int8_validation(L):
     assert d8(L, vs=ctypes.c_void_p(0x10002)) == ALIGN
     assert d8(L, kq=MIS) == ALIGN
     assert d8(L, ws=Z) == WORKSPACE
-    assert d8(L, q=Z, kq=Z, ks=Z, vq=Z, vs=Z, pt=Z, cl=Z, o=Z, lse=Z, ws=Z, S=0) == OK
+    assert d8(L, S=0) == SHAPE
+    assert d8(L, npages=0) == SHAPE
+
+
+def test_fwd_bf16_slice_limit(L):
+    # one (batch, head) slice of N x d bf16 values must span at most 2^32 - 1 bytes
+    assert fwd(L, "fa_fwd", N=2**24, d=128, B=1, Hq=1, Hkv=1) == SHAPE
+    assert fwd(L, "fa_fwd", N=2**24 - 1, d=128, B=1, Hq=1, Hkv=1, q=Z) == NULL
+    assert fwd(L, "fa_fwd", N=2**25, d=64, B=1, Hq=1, Hkv=1) == SHAPE
+    assert fwd(L, "fa_fwd", N=2**25 - 1, d=64, B=1, Hq=1, Hkv=1, q=Z) == NULL
+
+
+def test_workspace_sizes_reject_empty(L):
+    assert fa.fa_decode_paged_workspace_size(0, 8, 128, 4, 16) == 0
+    assert fa.fa_bwd_workspace_size(0, 2, 1, 16, 64) == 0
+    assert fa.fa_bwd_workspace_size(1, 2, 1, 0, 64) == 0

@@ -1,22 +1,19 @@
 """GPU parity of the INT8 group-scaled paged decode against the fp64 oracle (the decode
 definition on the dequantized cache), every element.  Bars as for the bf16 decode:
-O within 1e-2, L within 1e-3.  Slots past each context and the padding page carry NaN
+O within 1e-2, L within 1e-3, with the bf16 output-floor rule of tests/_parity.py.  Slots past each context and the padding page carry NaN
 scales (and arbitrary int8 values), so any leak fails the check."""
 
 import numpy as np
 import pytest
 import torch
 
+from _parity import check_bf16, say
 from exact_io_aware_15_amd import fa_decode_paged_int8
 from exact_io_aware_15_amd.workloads import make_decode_int8
 from oracle import decode_int8_ref
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
-
-
-def say(msg):
-    print(msg, flush=True)
 
 
 def run(x, scale=None):
@@ -35,14 +32,7 @@ def check(x, out, lse, what):
     Oref, Lref = decode_int8_ref(x["q"].double().numpy(), x["kq"].numpy(), x["kscale"].numpy(), x["vq"].numpy(),
                                  x["vscale"].numpy(), x["page_table"].numpy(), x["ctx_lens"].numpy(),
                                  1.0 / np.sqrt(d))
-    O, L = out.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
-    assert np.all(np.isfinite(O))
-    fin = np.isfinite(Lref)
-    assert np.all(np.isfinite(L[fin])) and np.all(np.isneginf(L[~fin]))
-    eo = float(np.max(np.abs(O - Oref)))
-    el = float(np.max(np.abs(L[fin] - Lref[fin]))) if fin.any() else 0.0
-    say(f"{what}: max|dO|={eo:.3e} max|dL|={el:.3e}")
-    assert eo <= 1e-2 and el <= 1e-3
+    check_bf16(out, lse, Oref, Lref, what)
 
 
 CASES = [

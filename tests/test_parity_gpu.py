@@ -1,32 +1,25 @@
 """GPU parity: the HIP library against the fp64 oracle, element by element.
 
 Bars: fp32 O and L within 1e-4; bf16 O within 1e-2 and L within 1e-3 (max-abs over
-every compared element).  Small shapes compare every output element; the full-size
-workloads compare sampled query rows (every head and batch) that the oracle can
-evaluate one by one, plus the properties that hold at any size.  Outputs are
-pre-filled with NaN, so an element the kernels never write fails the check.
+every element), with the bf16 output-floor rule of tests/_parity.py where the
+format's own half-ulp exceeds the bar.  Every test compares every output element,
+the full-size workloads included (the oracle evaluates them in row chunks), plus
+properties that hold at any size.  Outputs are pre-filled with NaN, so an element
+the kernels never write fails the check.
 """
 
 import numpy as np
 import pytest
 import torch
 
+from _parity import check_bf16, check_f32, f64, say
 from exact_io_aware_15_amd import fa_decode_paged, fa_fwd, fa_fwd_f32
 from exact_io_aware_15_amd.workloads import CONFIGS, make_decode, make_inputs, make_prefill
 from oracle import attention_ref, decode_ref
 
 pytestmark = pytest.mark.gpu
 
-TOL = {"f32": (1e-4, 1e-4), "bf16": (1e-2, 1e-3)}
 DEV = "cuda:0"
-
-
-def say(msg):
-    print(msg, flush=True)
-
-
-def f64(t):
-    return t.float().cpu().numpy().astype(np.float64)
 
 
 def gpu_prefill(x, causal, dtype, scale=None):
@@ -40,17 +33,7 @@ def gpu_prefill(x, causal, dtype, scale=None):
 
 
 def check(O, L, Oref, Lref, dtype, what):
-    tol_o, tol_l = TOL[dtype]
-    assert np.all(np.isfinite(O)), f"{what}: non-finite O"
-    assert np.all(np.isfinite(L) | np.isneginf(Lref)), f"{what}: non-finite L"
-    eo = float(np.max(np.abs(O - Oref))) if O.size else 0.0
-    fin = np.isfinite(Lref)
-    el = float(np.max(np.abs(L[fin] - Lref[fin]))) if fin.any() else 0.0
-    floor = float(np.max(np.abs(f64(torch.from_numpy(Oref).to(torch.bfloat16)) - Oref))) if dtype == "bf16" and O.size else 0.0
-    say(f"{what}: max|dO|={eo:.3e} (bf16 output floor {floor:.3e}) max|dL|={el:.3e}")
-    assert eo <= tol_o, f"{what}: O error {eo} > {tol_o}"
-    assert el <= tol_l, f"{what}: L error {el} > {tol_l}"
-    assert np.all(np.isneginf(L[~fin])), f"{what}: empty rows must have L = -inf"
+    return (check_bf16 if dtype == "bf16" else check_f32)(O, L, Oref, Lref, what)
 
 
 SMALL = [
@@ -95,8 +78,10 @@ def test_prefill_small_every_element(shape):
     check(f64(out), f64(lse), Oref, Lref, dtype, str(shape))
 
 
-@pytest.mark.parametrize("scale", [0.0, -0.0883883, 0.5])
+@pytest.mark.parametrize("scale", [0.0, -0.0883883, 0.5, 0.9])
 def test_prefill_scale_edge_cases(scale):
+    # zero, negative and large scales; at 0.9 the logits span tens of log2 units and the
+    # first causal rows average a few V rows, so |O| reaches the bf16 output floor
     say(f"prefill scale {scale}")
     x = make_prefill(1, 2, 1, 150, 128, "bf16", seed=7)
     for causal in (False, True):
@@ -125,29 +110,20 @@ def test_prefill_rising_logits(d, step):
         check(f64(out), f64(lse), Oref, Lref, "bf16", f"rising d={d} step={step} causal={causal}")
 
 
-def sample_rows(N, seed, extra=48):
-    rng = np.random.default_rng(seed)
-    fixed = [0, 1, 2, 3, 31, 32, 63, 64, 65, 127, 128, 255, 256, 257, 511, 512, N // 2, N - 2, N - 1]
-    rows = set(r for r in fixed if 0 <= r < N) | set(rng.choice(N, size=min(extra, N), replace=False).tolist())
-    return np.array(sorted(rows))
-
-
 PREFILL_CFGS = [n for n, c in CONFIGS.items() if c.kind == "prefill"]
 
 
 @pytest.mark.parametrize("name", PREFILL_CFGS)
-def test_prefill_full_size_sampled_rows(name):
+def test_prefill_full_size_every_element(name):
+    """Every element of O and L of the configuration, in the launch the bench times."""
     cfg = CONFIGS[name]
     say(f"full-size prefill {name}")
     x = make_inputs(cfg)
-    out, lse = gpu_prefill(x, cfg.causal, cfg.dtype)
-    rows = np.arange(cfg.N) if cfg.N <= 256 else sample_rows(cfg.N, cfg.seed)
-    Oref, Lref = attention_ref(f64(x["q"]), f64(x["k"]), f64(x["v"]), cfg.causal, cfg.scale, rows=rows)
-    O = f64(out[:, :, torch.from_numpy(rows).to(DEV)])
-    L = f64(lse[:, :, torch.from_numpy(rows).to(DEV)])
-    check(O, L, Oref, Lref, cfg.dtype, f"{name} ({len(rows)} rows x {cfg.B * cfg.Hq} heads)")
-    # every element written and finite, at every row
-    assert torch.isfinite(out).all().item() and torch.isfinite(lse).all().item()
+    out, lse = gpu_prefill(x, cfg.causal, cfg.dtype, scale=cfg.scale)
+    O, L = f64(out), f64(lse)
+    del out, lse
+    Oref, Lref = attention_ref(f64(x["q"]), f64(x["k"]), f64(x["v"]), cfg.causal, cfg.scale)
+    check(O, L, Oref, Lref, cfg.dtype, f"{name} (all {cfg.N} rows x {cfg.B * cfg.Hq} heads)")
 
 
 def test_prefill_gqa_equals_mha_on_repeated_kv_bitwise():

@@ -1,26 +1,19 @@
 """GPU parity of the chunked prefill over a paged cache (fa_prefill_paged) against
 the fp64 oracle, every element.  Bars as for the bf16 forward: O within 1e-2, L within
-1e-3.  The page pools carry NaN in every slot past a sequence's context and in the
+1e-3, with the bf16 output-floor rule of tests/_parity.py.  The page pools carry NaN in every slot past a sequence's context and in the
 padding page, so a read past the context fails the check."""
 
 import numpy as np
 import pytest
 import torch
 
+from _parity import check_bf16, f64, say
 from exact_io_aware_15_amd import fa_decode_paged, fa_prefill_paged
 from exact_io_aware_15_amd.workloads import make_prefill_paged
 from oracle import prefill_paged_ref
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
-
-
-def say(msg):
-    print(msg, flush=True)
-
-
-def f64(t):
-    return t.float().cpu().numpy().astype(np.float64)
 
 
 def run(x, scale=None):
@@ -56,11 +49,7 @@ def test_prefill_paged_every_element(case):
     x = make_prefill_paged(S, Hq, Hkv, d, C, 1, 64, seed=500 + C, fixed_ctx=lens)
     out, lse = run(x)
     Oref, Lref = oracle(x, 1.0 / np.sqrt(d))
-    O, L = f64(out), f64(lse)
-    assert np.all(np.isfinite(O)) and np.all(np.isfinite(L))
-    eo, el = float(np.max(np.abs(O - Oref))), float(np.max(np.abs(L - Lref)))
-    say(f"{case}: max|dO|={eo:.3e} max|dL|={el:.3e}")
-    assert eo <= 1e-2 and el <= 1e-3
+    check_bf16(out, lse, Oref, Lref, str(case))
 
 
 def test_prefill_paged_chunk_of_one_matches_decode():
@@ -79,8 +68,4 @@ def test_prefill_paged_full_size():
     x = make_prefill_paged(16, 32, 8, 128, 512, 512, 16384, seed=6)
     out, lse = run(x)
     Oref, Lref = oracle(x, 1.0 / np.sqrt(128))
-    O, L = f64(out), f64(lse)
-    assert np.all(np.isfinite(O)) and np.all(np.isfinite(L))
-    eo, el = float(np.max(np.abs(O - Oref))), float(np.max(np.abs(L - Lref)))
-    say(f"full: max|dO|={eo:.3e} max|dL|={el:.3e}")
-    assert eo <= 1e-2 and el <= 1e-3
+    check_bf16(out, lse, Oref, Lref, "full size (16 x 512-token chunks)")

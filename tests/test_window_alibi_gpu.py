@@ -1,28 +1,20 @@
 """GPU parity of the sliding-window / ALiBi forward (fa_fwd_ex) against the fp64 oracle.
 
-Same bars as the plain bf16 forward: O within 1e-2 and L within 1e-3 (max-abs).
-Small shapes compare every element; full-size workloads compare sampled rows
-(including rows whose window edge cuts a tile, and the first rows).  Outputs are
-pre-filled with NaN."""
+Same bars as the plain bf16 forward: O within 1e-2 and L within 1e-3 (max-abs),
+with the bf16 output-floor rule of tests/_parity.py.  Every test compares every
+output element, the full-size workloads included.  Outputs are pre-filled with NaN."""
 
 import numpy as np
 import pytest
 import torch
 
+from _parity import check_bf16, f64, say
 from exact_io_aware_15_amd import fa_fwd, fa_fwd_ex
 from exact_io_aware_15_amd.workloads import CONFIGS, make_alibi_slopes, make_inputs, make_prefill
 from oracle import attention_ref
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
-
-
-def say(msg):
-    print(msg, flush=True)
-
-
-def f64(t):
-    return t.float().cpu().numpy().astype(np.float64)
 
 
 def run_ex(x, causal, window, alibi, scale=None):
@@ -38,11 +30,7 @@ def run_ex(x, causal, window, alibi, scale=None):
 
 
 def check(O, L, Oref, Lref, what):
-    assert np.all(np.isfinite(O)) and np.all(np.isfinite(L)), f"{what}: non-finite output"
-    eo = float(np.max(np.abs(O - Oref))) if O.size else 0.0
-    el = float(np.max(np.abs(L - Lref))) if L.size else 0.0
-    say(f"{what}: max|dO|={eo:.3e} max|dL|={el:.3e}")
-    assert eo <= 1e-2 and el <= 1e-3, what
+    return check_bf16(O, L, Oref, Lref, what)
 
 
 SMALL = [
@@ -71,11 +59,13 @@ def test_window_alibi_small_every_element(shape):
     check(f64(out), f64(lse), Oref, Lref, str(shape))
 
 
-@pytest.mark.parametrize("scale", [0.0, -0.11, 0.3])
+@pytest.mark.parametrize("scale", [0.0, -0.11, 0.3, 0.9])
 @pytest.mark.parametrize("window", [0, 40])
 def test_causal_alibi_scale_edge_cases(scale, window):
     # zero, negative and large softmax scales with causal ALiBi (with and without a
-    # window): the bias enters independently of the scale's size and sign
+    # window): the bias enters independently of the scale's size and sign.  At 0.9 a
+    # few keys dominate each row and |O| reaches 4, where the bf16 output's own
+    # rounding exceeds 1e-2 (the output-floor rule applies there)
     say(f"causal alibi scale={scale} window={window}")
     x = make_prefill(1, 4, 2, 160, 128, "bf16", seed=57)
     out, lse, slopes = run_ex(x, True, window, True, scale=scale)
@@ -103,16 +93,13 @@ FULL = [
 
 
 @pytest.mark.parametrize("name,window,alibi", FULL, ids=[f"{f[0]}_w{f[1]}" for f in FULL])
-def test_window_alibi_full_size_sampled_rows(name, window, alibi):
+def test_window_alibi_full_size_every_element(name, window, alibi):
     cfg = CONFIGS[name]
     say(f"window/alibi full-size {name} window={window} alibi={alibi}")
     x = make_inputs(cfg)
     out, lse, slopes = run_ex(x, cfg.causal, window, alibi, scale=cfg.scale)
-    rng = np.random.default_rng(cfg.seed)
-    fixed = [0, 1, 63, 64, 255, 256, window - 1, window, window + 1, window + 63, cfg.N // 2, cfg.N - 1]
-    rows = np.array(sorted(set(r for r in fixed if 0 <= r < cfg.N) | set(rng.choice(cfg.N, 24, replace=False).tolist())))
-    Oref, Lref = attention_ref(f64(x["q"]), f64(x["k"]), f64(x["v"]), cfg.causal, cfg.scale, rows=rows,
-                               window=window, alibi_slopes=slopes)
-    ri = torch.from_numpy(rows).to(DEV)
-    check(f64(out[:, :, ri]), f64(lse[:, :, ri]), Oref, Lref, f"{name} window={window} alibi={alibi}")
-    assert torch.isfinite(out).all().item() and torch.isfinite(lse).all().item()
+    O, L = f64(out), f64(lse)
+    del out, lse
+    Oref, Lref = attention_ref(f64(x["q"]), f64(x["k"]), f64(x["v"]), cfg.causal, cfg.scale, window=window,
+                               alibi_slopes=slopes)
+    check(O, L, Oref, Lref, f"{name} window={window} alibi={alibi} (every element)")
