@@ -28,6 +28,8 @@ __all__ = [
     "fa_decode_paged_workspace_size",
     "fa_prefill_paged",
     "fa_decode_paged_int8",
+    "fa_decode_paged_noalloc",
+    "fa_decode_paged_noalloc_max_scratch",
     "fa_status_string",
     "LIB_PATH",
 ]
@@ -71,6 +73,10 @@ def lib() -> ctypes.CDLL:
     L.fa_decode_paged_workspace_size.restype = sz
     L.fa_decode_paged.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp, sz, vp]
     L.fa_decode_paged.restype = i
+    L.fa_decode_paged_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp]
+    L.fa_decode_paged_noalloc.restype = i
+    L.fa_decode_paged_noalloc_max_scratch.argtypes = []
+    L.fa_decode_paged_noalloc_max_scratch.restype = sz
     L.fa_status_string.argtypes = [i]
     L.fa_status_string.restype = ctypes.c_char_p
     _lib = L
@@ -235,6 +241,36 @@ def fa_decode_paged(q, kpages, vpages, page_table, ctx_lens, scale=None, out=Non
                                _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(q))
     if st != FA_OK:
         raise FAError(st, "fa_decode_paged")
+    return out, lse
+
+
+def fa_decode_paged_noalloc_max_scratch() -> int:
+    return int(lib().fa_decode_paged_noalloc_max_scratch())
+
+
+def fa_decode_paged_noalloc(q, kpages, vpages, page_table, ctx_lens, out, lse, scale=None):
+    """fa_decode_paged with the library's own device scratch instead of a workspace.  The
+    caller passes the outputs (O bf16 [S,Hq,d], L fp32 [S,Hq]); nothing is allocated."""
+    S, Hq, d = q.shape
+    P, Hkv, page_size, _ = kpages.shape
+    maxp = page_table.shape[1]
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on a GPU")
+    _need(q, "q", torch.bfloat16, (S, Hq, d), dev)
+    _need(kpages, "kpages", torch.bfloat16, (P, Hkv, page_size, d), dev)
+    _need(vpages, "vpages", torch.bfloat16, (P, Hkv, page_size, d), dev)
+    _need(page_table, "page_table", torch.int32, (S, maxp), dev)
+    _need(ctx_lens, "ctx_lens", torch.int32, (S,), dev)
+    _need(out, "out", torch.bfloat16, (S, Hq, d), dev)
+    _need(lse, "lse", torch.float32, (S, Hq), dev)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    st = lib().fa_decode_paged_noalloc(_ptr(q), _ptr(kpages), _ptr(vpages), _ptr(page_table), _ptr(ctx_lens),
+                                       _ptr(out), _ptr(lse), S, Hq, Hkv, d, page_size, maxp, P, float(scale),
+                                       _stream(q))
+    if st != FA_OK:
+        raise FAError(st, "fa_decode_paged_noalloc")
     return out, lse
 
 

@@ -228,6 +228,31 @@ int fa_decode_paged_int8(const void* q, const int8_t* kpages, const float* kscal
   return finish(fa::launch_decode_paged(a), stream);
 }
 
+int fa_decode_paged_noalloc(const void* q, const void* kpages, const void* vpages, const int32_t* page_table,
+                            const int32_t* ctx_lens, void* o, float* lse, int num_seqs, int Hq, int Hkv, int d,
+                            int page_size, int max_pages_per_seq, int num_pages, float scale, void* stream) {
+  if (num_seqs < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || max_pages_per_seq < 1 || num_pages < 1)
+    return FA_ERR_SHAPE;
+  if (check_decode_sizes(num_seqs, Hq, max_pages_per_seq) != FA_OK) return FA_ERR_SHAPE;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  if (page_size != 16) return FA_ERR_UNSUPPORTED;
+  if (!std::isfinite(scale)) return FA_ERR_SCALE;
+  if (!q || !kpages || !vpages || !page_table || !ctx_lens || !o || !lse) return FA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(kpages) || !aligned16(vpages) || !aligned16(page_table) ||
+      !aligned16(ctx_lens) || !aligned16(o) || !aligned16(lse))
+    return FA_ERR_ALIGN;
+  if (fa::decode_workspace_bytes(num_seqs, Hq, d, max_pages_per_seq) > fa::kNoAllocScratchBytes)
+    return FA_ERR_SCRATCH;
+  void* ws = nullptr;
+  const hipError_t e = fa::noalloc_scratch(stream, &ws);
+  if (e != hipSuccess) return hip_status(e);
+  fa::DecodeArgs a{q,  kpages, vpages, page_table, ctx_lens, o, lse, num_seqs, Hq, Hkv, d, page_size,
+                   max_pages_per_seq, num_pages, scale, ws, stream};
+  return finish(fa::launch_decode_paged(a), stream);
+}
+
+size_t fa_decode_paged_noalloc_max_scratch(void) { return fa::kNoAllocScratchBytes; }
+
 const char* fa_status_string(int status) {
   switch (status) {
     case FA_OK: return "ok";
@@ -238,6 +263,8 @@ const char* fa_status_string(int status) {
     case FA_ERR_ALIGN: return "a tensor pointer is not 16-byte aligned";
     case FA_ERR_WORKSPACE: return "decode workspace is NULL or too small";
     case FA_ERR_HIP: return g_hip_error;
+    case FA_ERR_SCRATCH:
+      return "sizes need more than the library's fixed device scratch (fa_decode_paged_noalloc_max_scratch bytes)";
     default: return "unknown status";
   }
 }

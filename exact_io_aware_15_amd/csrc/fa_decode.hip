@@ -26,6 +26,8 @@
 //
 // Phase 2 (decode_merge_kernel): per (sequence, query head) combine the splits:
 // L = log sum_c exp(lse_c), O = sum_c exp(lse_c - L) o_c.
+#include <mutex>
+
 #include "fa_device.h"
 #include "fa_launch.h"
 
@@ -674,10 +676,53 @@ hipError_t launch_d(const DecodeArgs& a) {
   return hipGetLastError();
 }
 
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
 }  // namespace
+
+// Device scratch of the allocation-free decode (fa_decode_paged_noalloc): the split
+// partials live here instead of in a caller workspace.  One copy per GPU, held until
+// the process ends; every call on a GPU shares it, so overlapping calls on one GPU
+// race.  The split kernels write every partial the merge kernel reads in the same
+// call, so nothing needs clearing between calls.
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
 
 hipError_t launch_decode_paged(const DecodeArgs& a) {
   return a.d == 64 ? launch_d<64>(a) : launch_d<128>(a);
+}
+
+// Device address of this GPU's scratch copy.  The array's name is a host-side
+// stand-in, not a device address, so the address is looked up once per device
+// (with that device current) and cached; kernels only ever get the cached pointer.
+hipError_t noalloc_scratch(void* stream, void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  int sdev = dev;
+  if (stream != nullptr) {
+    hipDevice_t d = 0;
+    e = hipStreamGetDevice((hipStream_t)stream, &d);
+    if (e != hipSuccess) return e;
+    sdev = (int)d;
+  }
+  if (sdev < 0 || sdev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[sdev] == nullptr) {
+    if (sdev != dev && (e = hipSetDevice(sdev)) != hipSuccess) return e;
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (sdev != dev) {
+      const hipError_t e2 = hipSetDevice(dev);
+      if (e == hipSuccess) e = e2;
+    }
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[sdev] = p;
+  }
+  *ptr = g_scratch_ptr[sdev];
+  return hipSuccess;
 }
 
 }  // namespace fa

@@ -126,4 +126,9 @@ hipError_t launch_bwd_bf16(const BwdArgs& a);
 hipError_t launch_fwd_f32(const FwdArgs& a);
 hipError_t launch_decode_paged(const DecodeArgs& a);
 
+// Allocation-free decode: the library's own device scratch replaces the workspace.
+constexpr size_t kNoAllocScratchBytes = size_t(32) << 20;  // 32 MiB per GPU
+// Device address of the scratch on the stream's GPU (looked up once per device).
+hipError_t noalloc_scratch(void* stream, void** ptr);
+
 }  // namespace fa

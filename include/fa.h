@@ -35,7 +35,9 @@
  *     (FA_ERR_UNSUPPORTED), scale (FA_ERR_SCALE), pointers (FA_ERR_NULL, then
  *     FA_ERR_ALIGN), workspace (FA_ERR_WORKSPACE).
  *   - Thread safety: the library has no mutable global state besides a
- *     thread-local copy of the last HIP error text.
+ *     thread-local copy of the last HIP error text and, for
+ *     fa_decode_paged_noalloc, its per-GPU device scratch and the cached device
+ *     addresses of that scratch (looked up under a lock).
  */
 #ifndef FA_MI355X_H
 #define FA_MI355X_H
@@ -56,6 +58,7 @@ extern "C" {
 #define FA_ERR_ALIGN       5 /* a tensor pointer is not 16-byte aligned            */
 #define FA_ERR_WORKSPACE   6 /* decode workspace NULL or smaller than required     */
 #define FA_ERR_HIP         7 /* a HIP launch / runtime call failed                 */
+#define FA_ERR_SCRATCH     8 /* sizes exceed the fixed scratch of a _noalloc call  */
 
 /*
  * fa_fwd -- bf16 exact-attention forward (prefill).
@@ -221,6 +224,32 @@ int fa_decode_paged(const void* q, const void* kpages, const void* vpages,
                     int num_seqs, int Hq, int Hkv, int d, int page_size,
                     int max_pages_per_seq, int num_pages, float scale,
                     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * fa_decode_paged_noalloc -- fa_decode_paged without a caller workspace, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation).
+ *
+ * Same operation, arguments, layouts and status codes as fa_decode_paged, minus
+ * workspace / workspace_bytes.  The split partials go to a device scratch array
+ * the library holds, one copy per GPU, of fa_decode_paged_noalloc_max_scratch()
+ * bytes (32 MiB), kept until the process ends.  Sizes whose workspace
+ * (fa_decode_paged_workspace_size) exceeds it return FA_ERR_SCRATCH and launch
+ * nothing.  The call itself allocates nothing: the scratch's device address is
+ * looked up once per device, on the first call that uses it.  Every call on a
+ * GPU shares that GPU's scratch: calls that overlap on one GPU (different streams,
+ * or different host threads without ordering) race and give wrong output; calls
+ * ordered on one stream are fine.
+ */
+int fa_decode_paged_noalloc(const void* q, const void* kpages, const void* vpages,
+                            const int32_t* page_table, const int32_t* ctx_lens,
+                            void* o, float* lse,
+                            int num_seqs, int Hq, int Hkv, int d, int page_size,
+                            int max_pages_per_seq, int num_pages, float scale,
+                            void* stream);
+
+/* Bytes of the device scratch behind fa_decode_paged_noalloc (per GPU). */
+size_t fa_decode_paged_noalloc_max_scratch(void);
 
 /*
  * fa_decode_paged_int8 -- fa_decode_paged over an INT8 KV cache with group-wise

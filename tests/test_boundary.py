@@ -11,7 +11,7 @@ import exact_io_aware_15_amd as fa
 
 HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "fa.h")
 
-OK, NULL, SHAPE, UNSUP, SCALE, ALIGN, WORKSPACE, HIP = range(8)
+OK, NULL, SHAPE, UNSUP, SCALE, ALIGN, WORKSPACE, HIP, SCRATCH = range(9)
 P = ctypes.c_void_p(0x10000)      # aligned stand-in device pointer, never dereferenced
 MIS = ctypes.c_void_p(0x10008)    # 8-byte aligned only
 Z = ctypes.c_void_p(0)
@@ -42,8 +42,9 @@ def test_status_codes_match_header(L):
     text = open(HEADER).read()
     codes = dict((k, int(v)) for k, v in re.findall(r"#define (FA_\w+)\s+(\d+)", text))
     assert codes == {"FA_OK": 0, "FA_ERR_NULL": 1, "FA_ERR_SHAPE": 2, "FA_ERR_UNSUPPORTED": 3,
-                     "FA_ERR_SCALE": 4, "FA_ERR_ALIGN": 5, "FA_ERR_WORKSPACE": 6, "FA_ERR_HIP": 7}
-    for c in range(8):
+                     "FA_ERR_SCALE": 4, "FA_ERR_ALIGN": 5, "FA_ERR_WORKSPACE": 6, "FA_ERR_HIP": 7,
+                     "FA_ERR_SCRATCH": 8}
+    for c in range(9):
         assert fa.fa_status_string(c)
     assert fa.fa_status_string(99) == "unknown status"
 
@@ -229,3 +230,26 @@ def test_workspace_sizes_reject_empty(L):
     assert fa.fa_decode_paged_workspace_size(0, 8, 128, 4, 16) == 0
     assert fa.fa_bwd_workspace_size(0, 2, 1, 16, 64) == 0
     assert fa.fa_bwd_workspace_size(1, 2, 1, 0, 64) == 0
+
+
+def na(L, q=P, kp=P, vp=P, pt=P, cl=P, o=P, lse=P, S=2, Hq=8, Hkv=2, d=128, ps=16, maxp=4, npages=9, scale=0.1):
+    return L.fa_decode_paged_noalloc(q, kp, vp, pt, cl, o, lse, S, Hq, Hkv, d, ps, maxp, npages, scale, Z)
+
+
+def test_decode_noalloc_validation(L):
+    assert na(L, q=Z) == NULL
+    assert na(L, d=80) == UNSUP
+    assert na(L, ps=32) == UNSUP
+    assert na(L, Hq=6, Hkv=4) == SHAPE
+    assert na(L, S=0) == SHAPE
+    assert na(L, scale=float("nan")) == SCALE
+    assert na(L, lse=MIS) == ALIGN
+    cap = L.fa_decode_paged_noalloc_max_scratch()
+    assert cap == 32 << 20
+    # sizes whose partials exceed the fixed scratch are rejected before any HIP call
+    S, Hq, d = 64, 32, 128
+    maxp = 128
+    while fa.fa_decode_paged_workspace_size(S, Hq, d, maxp) <= cap:
+        maxp += 128
+    assert na(L, S=S, Hq=Hq, Hkv=8, d=d, maxp=maxp) == SCRATCH
+    assert "scratch" in fa.fa_status_string(SCRATCH)
