@@ -227,12 +227,18 @@ struct AlibiExt {
 // copy), which lets the compiler drop the wait for all outstanding HBM -> LDS
 // copies that it would otherwise put before the first transposing V read.
 // RTMASK: plain path with the mask decided at run time by need_mask.
+// SPLIT (causal ALiBi, wave-uniform): the probabilities enter the P V product as two
+// bf16 parts, bf16(p) and bf16(p - bf16(p)), one MFMA each.  Used on the tiles nearest
+// a wave's diagonal, where steep slopes put almost all of a row's weight on a few
+// keys: the rounding of those few weights to bf16 (2^-9 relative) would otherwise
+// reach O directly, while over many keys the roundings average out.
 template <int D, bool MASK, bool EXT, bool LIN = false, bool RTMASK = false>
 __device__ __forceinline__ void process_tile(WaveState<D>& st, const uint8_t* __restrict__ kb,
                                              const uint8_t* __restrict__ vb,
                                              const int (&koff)[D / 16], const int (&voff)[D / 32], int lim,
                                              int l32, float c, int lo = 0, float base = 0.f, float slope2 = 0.f,
-                                             const AlibiExt* ax = nullptr, bool need_mask = false) {
+                                             const AlibiExt* ax = nullptr, bool need_mask = false,
+                                             bool split = false) {
   using LY = Lay<D>;
   constexpr int KK = D / 16;
   constexpr int DB = D / 32;
@@ -267,6 +273,7 @@ __device__ __forceinline__ void process_tile(WaveState<D>& st, const uint8_t* __
 
   // ---- online softmax
   bf16x8 pb[NA][2];
+  bf16x8 pbl[NA][2];  // SPLIT: second bf16 parts
   if constexpr (EXT && LIN) {
     // Causal: a visible key never lies after its row, so the ALiBi term
     // -slope2 |i - j| = slope2 (kofs + 4hi) - slope2 (base + 4hi) is affine in the key
@@ -304,6 +311,28 @@ __device__ __forceinline__ void process_tile(WaveState<D>& st, const uint8_t* __
         for (int r = 0; r < 16; ++r) sc[a][r] -= sh;
     }
     softmax_pack<D, true, true>(sc, st, 1.f, pb);
+    if (split) {
+      // the second bf16 part of each probability (p = exp2(y), as in softmax_pack)
+      const bf16x2 ones = as_bf16x2(0x3f803f80u);
+      float rlo = 0.f;
+#pragma unroll
+      for (int a = 0; a < NA; ++a)
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+          const u32x4 hk = __builtin_bit_cast(u32x4, pb[a][h2]);
+          u32x4 lk;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float p0 = exp2_fast(sc[a][h2 * 8 + 2 * j]);
+            const float p1 = exp2_fast(sc[a][h2 * 8 + 2 * j + 1]);
+            const uint32_t hw = hk[j];
+            lk[j] = pack_bf16x2(p0 - bf16lo_to_f32(hw), p1 - bf16hi_to_f32(hw));
+            rlo = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(lk[j]), ones, rlo, false);
+          }
+          pbl[a][h2] = __builtin_bit_cast(bf16x8, lk);
+        }
+      st.l_round += rlo;
+    }
   } else if constexpr (EXT) {
 #pragma unroll
     for (int a = 0; a < NA; ++a)
@@ -349,6 +378,24 @@ __device__ __forceinline__ void process_tile(WaveState<D>& st, const uint8_t* __
     __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
   }
   __builtin_amdgcn_sched_group_barrier(0x008, kPrefetch, 1);
+  if constexpr (EXT && LIN) {
+    if (split) {
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int a = 0; a < NA; ++a)
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+          for (int db = 0; db < DB; ++db) {
+            const uint8_t* p1 = vb + (a * 32 + h2 * 16) * LY::ROWB + voff[db];
+            const s16x4 vlo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS s16x4*)(p1));
+            const s16x4 vup = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS s16x4*)(p1 + 8 * LY::ROWB));
+            const s16x8 cat = __builtin_shufflevector(vlo, vup, 0, 1, 2, 3, 4, 5, 6, 7);
+            st.oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, cat), pbl[a][h2],
+                                                                  st.oacc[db], 0, 0, 0);
+          }
+    }
+  }
 }
 
 // HBM -> LDS copy of one K/V tile into buffer buf: this wave's 1 KB blocks
@@ -587,6 +634,7 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void fwd_bf16_kernel(
   wait_vmem_tiles<kLoadsPerTile>(min(kStages - 2, ntiles - 1 - t_begin));  // the first tile has landed
   __syncthreads();
 
+  int ndone = 0;  // tiles this wave has processed (EXT)
   // The loop is unrolled by kStages so every slot index, and with it every LDS
   // address offset, is a compile-time constant.
   for (int t0 = t_begin; t0 < ntiles; t0 += kStages) {
@@ -618,10 +666,16 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void fwd_bf16_kernel(
           // window: key visible iff koff + 4*hi >= qrow - window + 1 - j0
           const int lo = window > 0 ? qrowp - window + 1 - j0 - 4 * hi : -LY::BC;
           const float base = (float)(qrowp - j0 - 4 * hi);
+          // causal ALiBi: the first two tiles a wave takes (its diagonal tile and the one
+          // left of it, in the diagonal-first order) carry P in two bf16 parts
+          const bool split = rev && ndone < 2;
+          ++ndone;
           if (need_mask)
-            process_tile<D, true, true, CAUSAL>(st, kb, vb, koff, voff, lim, l32, c, lo, base, slope2, &ax);
+            process_tile<D, true, true, CAUSAL>(st, kb, vb, koff, voff, lim, l32, c, lo, base, slope2, &ax, false,
+                                                split);
           else
-            process_tile<D, false, true, CAUSAL>(st, kb, vb, koff, voff, lim, l32, c, lo, base, slope2, &ax);
+            process_tile<D, false, true, CAUSAL>(st, kb, vb, koff, voff, lim, l32, c, lo, base, slope2, &ax, false,
+                                                 split);
         } else {
           if constexpr (!CAUSAL) {
             // only a ragged last tile is masked

@@ -103,3 +103,22 @@ def test_window_alibi_full_size_every_element(name, window, alibi):
     Oref, Lref = attention_ref(f64(x["q"]), f64(x["k"]), f64(x["v"]), cfg.causal, cfg.scale, window=window,
                                alibi_slopes=slopes)
     check(O, L, Oref, Lref, f"{name} window={window} alibi={alibi} (every element)")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("window", [0, 300])
+def test_causal_alibi_steep_slopes_every_element(d, window):
+    """Slopes 2, 1, 0.5, 0.25: a row's weight sits on its last few keys, so the bf16
+    rounding of those few probabilities would reach O undamped (it averages out over
+    many keys).  The tiles nearest each wave's diagonal carry P in two bf16 parts."""
+    say(f"causal alibi steep slopes d={d} window={window}")
+    x = make_prefill(2, 4, 2, 700, d, "bf16", seed=71 + d + window)
+    q, k, v = (x[n].to(DEV) for n in "qkv")
+    slopes = torch.tensor([2.0, 1.0, 0.5, 0.25], dtype=torch.float32)
+    out = torch.full(q.shape, float("nan"), dtype=q.dtype, device=DEV)
+    lse = torch.full(q.shape[:3], float("nan"), dtype=torch.float32, device=DEV)
+    fa_fwd_ex(q, k, v, causal=True, window=window, alibi_slopes=slopes.to(DEV), out=out, lse=lse)
+    torch.cuda.synchronize()
+    Oref, Lref = attention_ref(f64(x["q"]), f64(x["k"]), f64(x["v"]), True, 1.0 / np.sqrt(d), window=window,
+                               alibi_slopes=slopes.double().numpy())
+    check(out, lse, Oref, Lref, f"steep slopes d={d} window={window}")
