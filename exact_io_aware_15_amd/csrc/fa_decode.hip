@@ -42,11 +42,43 @@ constexpr int kDecThreads = kDecWaves * 64;
 static_assert(kDecThreads == kGeomDecThreads, "host-side launch limits assume this workgroup size");
 
 __device__ __forceinline__ u32x4 ldg16(const uint16_t* p) { return *reinterpret_cast<const u32x4*>(p); }
-// Cache pages are read exactly once per call: the loads carry the non-temporal hint
-// (global_load ... nt), so streaming them does not evict what is reused.
-template <typename T>
-__device__ __forceinline__ T ld_stream(const void* p) {
-  return __builtin_nontemporal_load(reinterpret_cast<const T*>(p));
+
+// Page id of split page idx (wave-uniform, 0 <= idx < kDecodePagesPerSplit): lane i
+// of register r holds page p_begin + 64 r + i; read back with readlane.
+template <int R>
+__device__ __forceinline__ int page_id_of(const int (&lane_pid)[R], int idx) {
+  int id = __builtin_amdgcn_readlane(lane_pid[0], idx & 63);
+#pragma unroll
+  for (int r = 1; r < R; ++r)
+    if ((idx >> 6) == r) id = __builtin_amdgcn_readlane(lane_pid[r], idx & 63);
+  return id;
+}
+
+// This lane's K and V data of one (page, K/V head) block of BYTES bytes: NV 16-byte
+// loads at byte offsets off[i], non-temporal (each page is read once per call).  The
+// buffer descriptor spans the block, or nothing when the page lies past the split:
+// such loads return zeros without touching memory, so the loop's loads stay
+// unconditional (the compiler never has to drain the other buffer's loads early)
+// without fetching any page twice.
+template <int NV, typename T>
+__device__ __forceinline__ void load_block(const void* kblk, const void* vblk, uint32_t bytes, const int (&off)[NV],
+                                           T (&kd)[NV], T (&vd)[NV]) {
+  const auto krs = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(kblk), (short)0, bytes, 0x00020000);
+  const auto vrs = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(vblk), (short)0, bytes, 0x00020000);
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int o = off[i];
+    if constexpr (sizeof(T) == 16) {
+      kd[i] = __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b128(krs, o, 0, 2));
+      vd[i] = __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b128(vrs, o, 0, 2));
+    } else if constexpr (sizeof(T) == 8) {
+      kd[i] = __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b64(krs, o, 0, 2));
+      vd[i] = __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b64(vrs, o, 0, 2));
+    } else {
+      kd[i] = __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b32(krs, o, 0, 2));
+      vd[i] = __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b32(vrs, o, 0, 2));
+    }
+  }
 }
 
 template <int D, int HB>
@@ -126,41 +158,34 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
     const int id = pg < p_end ? trow[pg] : 0;
     lane_pid[r] = (unsigned)id < (unsigned)num_pages ? id : num_pages - 1;
   }
-  auto page_id = [&](int idx) {  // idx wave-uniform, 0 <= idx < kDecodePagesPerSplit
-    int id = __builtin_amdgcn_readlane(lane_pid[0], idx & 63);
-#pragma unroll
-    for (int r = 1; r < kIdRegs; ++r)
-      if ((idx >> 6) == r) id = __builtin_amdgcn_readlane(lane_pid[r], idx & 63);
-    return id;
-  };
   const size_t head_off = (size_t)g * kPage * D;
   const size_t page_stride = (size_t)Hkv * kPage * D;
+  // this lane's byte offsets in a (page, head) block: tokens 2 tg + j, columns (dg + 8 cc) * 8 ..
+  int boff[2 * CPL];
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int cc = 0; cc < CPL; ++cc) boff[j * CPL + cc] = ((2 * tg + j) * D + (dg + 8 * cc) * 8) * 2;
 
   // Two register buffers (A, B) of one page pair each, used alternately: the pair
   // after next is fetched into the buffer just consumed, so one pair is always in
   // flight while the other is processed (no register copies that would force a
-  // wait on outstanding loads).
-  u32x4 ka[PP][2][CPL], va[PP][2][CPL];
-  u32x4 kb[PP][2][CPL], vb[PP][2][CPL];
-  // Loads are unconditional (so the compiler keeps the other buffer's loads in
-  // flight across the waits): a page past this split's end is redirected to the
-  // split's last page, and its tokens are treated as invalid by consume().
-  auto fetch = [&](int p0, u32x4 (&kd)[PP][2][CPL], u32x4 (&vd)[PP][2][CPL]) {
+  // wait on outstanding loads).  A page past this split's end (the second page of an
+  // odd last pair, or the prefetch after a wave's last pair) gets an empty buffer
+  // descriptor: its loads return zeros without a memory access, and consume() treats
+  // its tokens as invalid.
+  u32x4 ka[PP][2 * CPL], va[PP][2 * CPL];
+  u32x4 kb[PP][2 * CPL], vb[PP][2 * CPL];
+  auto fetch = [&](int p0, u32x4 (&kd)[PP][2 * CPL], u32x4 (&vd)[PP][2 * CPL]) {
 #pragma unroll
     for (int pp = 0; pp < PP; ++pp) {
-      const int p = min(p0 + pp, p_end - 1);
-      const size_t base = (size_t)page_id(p - p_begin) * page_stride + head_off;
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int cc = 0; cc < CPL; ++cc) {
-          const size_t off = base + (size_t)(2 * tg + j) * D + (dg + 8 * cc) * 8;
-          kd[pp][j][cc] = ld_stream<u32x4>(KPg + off);
-          vd[pp][j][cc] = ld_stream<u32x4>(VPg + off);
-        }
+      const int p = p0 + pp;
+      const bool valid = p < p_end;
+      const size_t base = (size_t)page_id_of(lane_pid, min(p, p_end - 1) - p_begin) * page_stride + head_off;
+      load_block<2 * CPL>(KPg + base, VPg + base, valid ? kPage * D * 2 : 0, boff, kd[pp], vd[pp]);
     }
   };
-  auto consume = [&](int p, u32x4 (&kc)[PP][2][CPL], u32x4 (&vc)[PP][2][CPL]) {
+  auto consume = [&](int p, u32x4 (&kc)[PP][2 * CPL], u32x4 (&vc)[PP][2 * CPL]) {
     // scores: this lane's 2 tokens of each page of the pair, every served head
     float sc[PP][2][HB];
 #pragma unroll
@@ -176,7 +201,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
           for (int cc = 0; cc < CPL; ++cc)
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-              part = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(kc[pp][j][cc][e]), as_bf16x2(qp[hh][cc * 4 + e]),
+              part = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(kc[pp][j * CPL + cc][e]), as_bf16x2(qp[hh][cc * 4 + e]),
                                                      part, false);
           part = sum8(part) * qscale[hh];
           sc[pp][j][hh] = valid ? part : -INFINITY;
@@ -214,7 +239,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
 #pragma unroll
           for (int cc = 0; cc < CPL; ++cc)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) vc[pp][j][cc][e] = valid ? vc[pp][j][cc][e] : 0u;
+            for (int e = 0; e < 4; ++e) vc[pp][j * CPL + cc][e] = valid ? vc[pp][j * CPL + cc][e] : 0u;
         }
     }
     // O += P V as bf16 pair dot products over the lane's two tokens: P packed as
@@ -236,7 +261,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
       for (int cc = 0; cc < CPL; ++cc)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const uint32_t w0 = vc[pp][0][cc][e], w1 = vc[pp][1][cc][e];
+          const uint32_t w0 = vc[pp][cc][e], w1 = vc[pp][CPL + cc][e];
           const uint32_t lo = __builtin_amdgcn_perm(w1, w0, 0x05040100u);  // (w0.lo, w1.lo)
           const uint32_t hi = __builtin_amdgcn_perm(w1, w0, 0x07060302u);  // (w0.hi, w1.hi)
 #pragma unroll
@@ -254,13 +279,12 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
   constexpr int kStride = PP * kDecWaves;
   int p = p_begin + PP * w;
   if (p < p_end) fetch(p, ka, va);
-  // (the prefetch after a wave's last pair re-reads that pair, from L2)
   while (p < p_end) {
-    fetch(p + kStride < p_end ? p + kStride : p, kb, vb);
+    fetch(p + kStride, kb, vb);
     consume(p, ka, va);
     p += kStride;
     if (p >= p_end) break;
-    fetch(p + kStride < p_end ? p + kStride : p, ka, va);
+    fetch(p + kStride, ka, va);
     consume(p, kb, vb);
     p += kStride;
   }
@@ -434,30 +458,25 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_int8_kernel(
     const int id = pg < p_end ? trow[pg] : 0;
     lane_pid[r] = (unsigned)id < (unsigned)num_pages ? id : num_pages - 1;
   }
-  auto page_id = [&](int idx) {
-    int id = __builtin_amdgcn_readlane(lane_pid[0], idx & 63);
+  // this lane's byte offsets in a (page, head) block of int8 values and of scales
+  int boff[2], soff[2];
 #pragma unroll
-    for (int r = 1; r < kIdRegs; ++r)
-      if ((idx >> 6) == r) id = __builtin_amdgcn_readlane(lane_pid[r], idx & 63);
-    return id;
-  };
-
+  for (int j = 0; j < 2; ++j) {
+    boff[j] = (2 * tg + j) * D + dg * CH;
+    soff[j] = ((2 * tg + j) * NG + grp) * 4;
+  }
+  // as in decode_split_kernel: a page past the split gets empty buffer descriptors
   vec_t ka[PP][2], va[PP][2], kb[PP][2], vb[PP][2];
   float ksa[PP][2], vsa[PP][2], ksb[PP][2], vsb[PP][2];
   auto fetch = [&](int p0, vec_t (&kd)[PP][2], vec_t (&vd)[PP][2], float (&ksd)[PP][2], float (&vsd)[PP][2]) {
 #pragma unroll
     for (int pp = 0; pp < PP; ++pp) {
-      const int p = min(p0 + pp, p_end - 1);
-      const size_t head = (size_t)page_id(p - p_begin) * Hkv + g;
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int tok = 2 * tg + j;
-        const size_t off = (head * kPage + tok) * D + dg * CH;
-        kd[pp][j] = ld_stream<vec_t>(KQ + off);
-        vd[pp][j] = ld_stream<vec_t>(VQ + off);
-        ksd[pp][j] = ld_stream<float>(KS + (head * kPage + tok) * NG + grp);
-        vsd[pp][j] = ld_stream<float>(VS + (head * kPage + tok) * NG + grp);
-      }
+      const int p = p0 + pp;
+      const bool valid = p < p_end;
+      const size_t head = (size_t)page_id_of(lane_pid, min(p, p_end - 1) - p_begin) * Hkv + g;
+      load_block<2>(KQ + head * kPage * D, VQ + head * kPage * D, valid ? kPage * D : 0, boff, kd[pp], vd[pp]);
+      load_block<2>(KS + head * kPage * NG, VS + head * kPage * NG, valid ? kPage * NG * 4 : 0, soff, ksd[pp],
+                    vsd[pp]);
     }
   };
   auto consume = [&](int p, vec_t (&kc)[PP][2], vec_t (&vc)[PP][2], float (&ksc)[PP][2], float (&vsc)[PP][2]) {
@@ -549,11 +568,11 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_int8_kernel(
   int p = p_begin + PP * w;
   if (p < p_end) fetch(p, ka, va, ksa, vsa);
   while (p < p_end) {
-    fetch(p + kStride < p_end ? p + kStride : p, kb, vb, ksb, vsb);
+    fetch(p + kStride, kb, vb, ksb, vsb);
     consume(p, ka, va, ksa, vsa);
     p += kStride;
     if (p >= p_end) break;
-    fetch(p + kStride < p_end ? p + kStride : p, ka, va, ksa, vsa);
+    fetch(p + kStride, ka, va, ksa, vsa);
     consume(p, kb, vb, ksb, vsb);
     p += kStride;
   }
