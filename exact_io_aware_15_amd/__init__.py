@@ -19,6 +19,9 @@ import torch
 __all__ = [
     "FAError",
     "lib",
+    "load_library",
+    "use_library",
+    "DEBUG_SYNC_LIB_PATH",
     "fa_fwd",
     "fa_fwd_f32",
     "fa_fwd_ex",
@@ -35,9 +38,13 @@ __all__ = [
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
+# the same library built with every HBM -> LDS copy and LDS read stage fenced (tests
+# compare it bitwise with libfa.so)
+DEBUG_SYNC_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa_debugsync.so")
 
 FA_OK = 0
 _lib = None
+_loaded = {}
 
 
 class FAError(RuntimeError):
@@ -47,13 +54,39 @@ class FAError(RuntimeError):
 
 
 def lib() -> ctypes.CDLL:
-    """Load libfa.so (once).  Raises if it has not been built."""
+    """The library every call below uses: libfa.so, loaded once.  Raises if it has not
+    been built."""
     global _lib
-    if _lib is not None:
-        return _lib
-    if not os.path.exists(LIB_PATH):
-        raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m exact_io_aware_15_amd.build`")
-    L = ctypes.CDLL(LIB_PATH)
+    if _lib is None:
+        _lib = load_library(LIB_PATH)
+    return _lib
+
+
+class use_library:
+    """Context manager: route the calls of this module through another build of the
+    library (for instance load_library(DEBUG_SYNC_LIB_PATH)) inside the block."""
+
+    def __init__(self, L: ctypes.CDLL):
+        self.L = L
+
+    def __enter__(self):
+        global _lib
+        self.prev, _lib = lib(), self.L
+        return self.L
+
+    def __exit__(self, *exc):
+        global _lib
+        _lib = self.prev
+        return False
+
+
+def load_library(path: str) -> ctypes.CDLL:
+    """Load a build of the C ABI (once per path) and declare its signatures."""
+    if path in _loaded:
+        return _loaded[path]
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m exact_io_aware_15_amd.build`")
+    L = ctypes.CDLL(path)
     vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     L.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp]
     L.fa_fwd.restype = i
@@ -79,7 +112,7 @@ def lib() -> ctypes.CDLL:
     L.fa_decode_paged_noalloc_max_scratch.restype = sz
     L.fa_status_string.argtypes = [i]
     L.fa_status_string.restype = ctypes.c_char_p
-    _lib = L
+    _loaded[path] = L
     return L
 
 

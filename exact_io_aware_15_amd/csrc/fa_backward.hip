@@ -266,6 +266,7 @@ __global__ __launch_bounds__(kDqWaves * 64, 1) void bwd_dq_kernel(
         copy_tile<D, kDqWaves>(smem + (1 - u) * L::TBYTES, kbase, head_bytes, cp, j0 + kTile, w);
         copy_tile<D, kDqWaves>(smem + (3 - u) * L::TBYTES, vbase, head_bytes, cp, j0 + kTile, w);
       }
+      debug_copy_fence();
       const bool skip = CAUSAL && (j0 > rw0 + kWaveRows - 1);
       // restrict LDS tile pointers: the copy in flight writes only the other buffer,
       // so the reads need not wait for it (the compiler otherwise waits for all
@@ -295,6 +296,7 @@ __global__ __launch_bounds__(kDqWaves * 64, 1) void bwd_dq_kernel(
             dp[a] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, gf[kk], dp[a], 0, 0, 0);
           }
         sched_reads_ahead<4 * KK, 1, 0, kAhead>();
+        debug_read_fence();
         // exponents cs * s - l2 in place; masked keys (after the row, or past N) get
         // -inf in a branch that only tiles on the diagonal or past N take (the empty
         // asm keeps it a branch; selected into every tile the masking would cost
@@ -346,6 +348,7 @@ __global__ __launch_bounds__(kDqWaves * 64, 1) void bwd_dq_kernel(
                                                                 0, 0, 0);
             }
         sched_reads_ahead<4 * DB, 2, 1, kAhead>();
+        debug_read_fence();
       };
       if (!skip) tile(smem + u * L::TBYTES, smem + (2 + u) * L::TBYTES);
       __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): tile t+1 has landed
@@ -453,6 +456,7 @@ __device__ __forceinline__ void dkdv_tile(RP qb_, RP gb_, RF lrow, RF drow, bool
     dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga, vk, dp, 0, 0, 0);
   }
   sched_reads_ahead<2 * KK, kVinLds<D> ? 2 : 1, 2, kAhead>();
+  debug_read_fence();
   bf16x8 pb[2], dsb[2];
   if constexpr (D == 64) {
     // exponents s * cs - L2 in place (L2 = L log2 e); masked entries (key after the
@@ -539,6 +543,7 @@ __device__ __forceinline__ void dkdv_tile(RP qb_, RP gb_, RF lrow, RF drow, bool
       dka[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dsb[s2], tr_frag(qb_ + r0g, tlo[db], thi[db]), dka[db], 0, 0, 0);
     }
   sched_reads_ahead<4 * DB, 2, 3, kAhead>();
+  debug_read_fence();
 }
 
 // ---------------------------------------------------------------------------
@@ -667,6 +672,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(
     constexpr bool MASK = decltype(mask_c)::value;
     constexpr int u = decltype(u_c)::value;
     if (item + 1 < total) issue_item<D>(src, u ? smq0 : smq1, u ? smg0 : smg1, rowv, item + 1, 1 - u);
+    debug_copy_fence();
     int h, t;
     item_pos(src, item, h, t);
     const int rbase = t * kTile + rh * kWaveRows;  // the half's rows: rbase + 8j + 4hi + i

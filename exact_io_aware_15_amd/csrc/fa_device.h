@@ -45,6 +45,34 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
+// ---- debug-sync build ----------------------------------------------------------
+// Built with FA_DEBUG_SYNC=1 (libfa_debugsync.so), the tiled kernels wait for every
+// HBM -> LDS copy and fence it with a workgroup barrier as soon as it is issued, and
+// wait for every group of LDS fragment reads before the next stage.  The fast build
+// relies on its per-tile waits alone; the two builds must give bitwise equal results,
+// which a GPU test checks.
+#ifndef FA_DEBUG_SYNC
+#define FA_DEBUG_SYNC 0
+#endif
+// After a workgroup-uniform copy issue point: this wave's copies have landed, and so
+// have every other wave's (barrier).
+__device__ __forceinline__ void debug_copy_fence() {
+  if constexpr (FA_DEBUG_SYNC) {
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+// After a stage of LDS reads (per wave): every read has returned.
+__device__ __forceinline__ void debug_read_fence() {
+  if constexpr (FA_DEBUG_SYNC) {
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
 // ---- DPP / permlane cross-lane moves ------------------------------------------
 // DPP control words (gfx9): quad_perm [1,0,3,2] = 0xB1, [2,3,0,1] = 0x4E,
 // row_half_mirror = 0x141, row_ror:8 = 0x128.

@@ -270,6 +270,7 @@ __device__ __forceinline__ void process_tile(WaveState<D>& st, const uint8_t* __
     __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
   }
   __builtin_amdgcn_sched_group_barrier(0x008, kPrefetch, 0);
+  debug_read_fence();
 
   // ---- online softmax
   bf16x8 pb[NA][2];
@@ -378,6 +379,7 @@ __device__ __forceinline__ void process_tile(WaveState<D>& st, const uint8_t* __
     __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
   }
   __builtin_amdgcn_sched_group_barrier(0x008, kPrefetch, 1);
+  debug_read_fence();
   if constexpr (EXT && LIN) {
     if (split) {
       __builtin_amdgcn_sched_barrier(0);
@@ -651,6 +653,7 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void fwd_bf16_kernel(
           copy_tile<D>(smem, kbase, vbase, head_bytes, kcp, vcp, rev ? j0 - kAhead : j0 + kAhead,
                        (u + kStages - 1) % kStages, w);
       }
+      debug_copy_fence();
 
       const bool left_of_window = EXT && window > 0 && (j0 + LY::BC - 1 < rw0p - window + 1);
       const bool skip = (CAUSAL && (j0 > rw0p + kRowsPerWave - 1)) || left_of_window;
