@@ -345,9 +345,14 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
 //  - Keys: byte b enters as the fp16 value 1024 + (b + 128), built by one byte permute per channel pair (b ^ 0x80 as the
 //    low byte under a 0x64 high byte), against q converted exactly to fp16 under a power-of-two scale per head.  Then
 //    q.k = sum q_c (1152 + b_c) - 1152 sum q_c, with fp16 pair dot products and fp32 sums (the products are exact).
-//  - Values: byte b enters as the bf16 value b + 128 (exact for 1 .. 255), so O += p s (b + 128) - 128 p s per group,
-//    with bf16 pair dot products.  p s enters P V rounded to bf16, and O is normalised by the sum of the rounded
-//    probabilities, L by the fp32 sum.  (fp16 would bound p s to its range, which arbitrary scales need not respect.)
+//  - Values: byte b enters as the bf16 value b + 128 (exact for 1 .. 255: the fp32 conversion's upper half), so
+//    O += p s (b + 128) - 128 p s per group, with bf16 pair dot products.  p s enters P V rounded to bf16; O and L are
+//    normalised by the fp32 sum of the probabilities.  (fp16 would bound p s to its range, which arbitrary scales need
+//    not respect.)
+//  - Softmax: each lane keeps its own running maximum of the raw scores q.k * kscale (the factor k = |scale| log2(e)
+//    times the head's q unscale enters the exponent's fused multiply-add), raised only when a score passes it by more
+//    than 8 / k, so probabilities stay at most 2^8 and no per-page reduction across lanes is needed.  The lanes'
+//    maxima are combined once, after the loop.
 template <int CH>
 struct I8Vec;
 template <>
@@ -359,6 +364,13 @@ struct I8Vec<8> {
   typedef u32x2 T;
 };
 
+// Keeps the compiler from re-fusing a product into the following cross-lane add
+// (it would otherwise recompute the product in an fmac beside a DPP move).
+__device__ __forceinline__ float opaque(float x) {
+  asm("" : "+v"(x));
+  return x;
+}
+
 template <int D, int HB>
 __global__ __launch_bounds__(kDecThreads) void decode_split_int8_kernel(
     const uint16_t* __restrict__ Q, const int8_t* __restrict__ KQ, const float* __restrict__ KS,
@@ -369,10 +381,10 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_int8_kernel(
   constexpr int NG = D / 32;          // scale groups per token
   constexpr int NW = CH / 4;          // 32-bit words per token per lane
   constexpr int PP = 2;               // pages consumed per wave iteration
+  constexpr float kGrow = 8.f;        // log2 units a score may exceed the running max by
   typedef typename I8Vec<CH>::T vec_t;
   __shared__ float sm_m[kDecWaves][HB];
   __shared__ float sm_l[kDecWaves][HB];
-  __shared__ float sm_lr[kDecWaves][HB];
   __shared__ float sm_acc[kDecWaves][HB][D];
 
   const int split = blockIdx.y;
@@ -399,10 +411,12 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_int8_kernel(
   // q as fp16 channel pairs (the score dot2 operands) for the lane's channels.  Each
   // head's q is scaled by a power of two that puts its largest magnitude in
   // [2^13, 2^14), so every bf16 value converts to fp16 exactly (11 significant bits),
-  // and the score is scaled back by qunscale.  qsum = 1152 * sum q removes the key
-  // offset (see below).
+  // and negated when the softmax scale is negative, so that k >= 0.  qsum = 1152 *
+  // sum q removes the key offset (see above).
+  const float cabs = fabsf(c);
+  const float csgn = c < 0.f ? -1.f : 1.f;
   uint32_t qp[HB][CH / 2];
-  float qsum[HB], qunscale[HB];
+  float qsum[HB], kh[HB], grow_by[HB];
 #pragma unroll
   for (int hh = 0; hh < HB; ++hh) {
     const int hl = hb * HB + hh;
@@ -423,8 +437,9 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_int8_kernel(
     mx = fmaxf(mx, dpp<0x4E>(mx));
     mx = fmaxf(mx, dpp<0x141>(mx));
     const int ex = min(max(__builtin_amdgcn_frexp_expf(mx), -100), 128);  // mx in [2^(ex-1), 2^ex)
-    const float up = ldexpf(1.f, 14 - ex);
-    qunscale[hh] = ldexpf(1.f, ex - 14);
+    const float up = csgn * ldexpf(1.f, 14 - ex);
+    kh[hh] = cabs * ldexpf(1.f, ex - 14);
+    grow_by[hh] = kGrow / kh[hh];  // +inf when k = 0: the first maximum is kept
     float sum = 0.f;
 #pragma unroll
     for (int i = 0; i < CH / 2; ++i) {
@@ -436,14 +451,15 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_int8_kernel(
     qsum[hh] = 1152.f * sum;
   }
 
-  // running max, sums of the fp32 probabilities (L) and of their bf16 roundings (O),
-  // the offset correction and the unnormalised output accumulator
-  float m_run[HB], l_run[HB], l_rnd[HB], corr[HB], acc[HB][CH];
+  // per lane: running max of the raw scores, the score that triggers a rescale, -max*k,
+  // the fp32 probability sum, the offset correction and the unnormalised output
+  float m_run[HB], thr[HB], nmk[HB], l_run[HB], corr[HB], acc[HB][CH];
 #pragma unroll
   for (int hh = 0; hh < HB; ++hh) {
     m_run[hh] = -INFINITY;
+    thr[hh] = -INFINITY;
+    nmk[hh] = 0.f;
     l_run[hh] = 0.f;
-    l_rnd[hh] = 0.f;
     corr[hh] = 0.f;
 #pragma unroll
     for (int i = 0; i < CH; ++i) acc[hh][i] = 0.f;
@@ -480,7 +496,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_int8_kernel(
     }
   };
   auto consume = [&](int p, vec_t (&kc)[PP][2], vec_t (&vc)[PP][2], float (&ksc)[PP][2], float (&vsc)[PP][2]) {
-    float sc[PP][2][HB];
+    float sc[PP][2][HB];  // raw scores (q.k * kscale), -inf past the context
 #pragma unroll
     for (int pp = 0; pp < PP; ++pp)
 #pragma unroll
@@ -503,59 +519,64 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_int8_kernel(
           for (int i = 0; i < CH / 2; ++i)
             part = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, qp[hh][i]), __builtin_bit_cast(f16x2, up[i]), part,
                                           false);
-          part = sum8(part * ksc[pp][j]) * (c * qunscale[hh]);
+          // lanes l and l ^ 1 hold halves of one scale group (CH = 16) or of its first
+          // half (CH = 8): add them, apply the token's group scale, finish the sum
+          part += dpp<0xB1>(part);
+          part = opaque(part * ksc[pp][j]);
+          part += dpp<0x4E>(part);
+          part += dpp<0x141>(part);
           sc[pp][j][hh] = valid ? part : -INFINITY;
         }
       }
+    // raise a lane's max (and rescale its sums) only where a score passes the threshold
     bool grow = false;
-    float mnew[HB];
+    float pm[HB];
 #pragma unroll
     for (int hh = 0; hh < HB; ++hh) {
-      float pm = fmaxf(sc[0][0][hh], sc[0][1][hh]);
+      pm[hh] = fmaxf(sc[0][0][hh], sc[0][1][hh]);
 #pragma unroll
-      for (int pp = 1; pp < PP; ++pp) pm = fmaxf(pm, fmaxf(sc[pp][0][hh], sc[pp][1][hh]));
-      pm = max_stride8(pm);
-      mnew[hh] = fmaxf(m_run[hh], pm);
-      grow |= mnew[hh] > m_run[hh];
+      for (int pp = 1; pp < PP; ++pp) pm[hh] = fmaxf(pm[hh], fmaxf(sc[pp][0][hh], sc[pp][1][hh]));
+      grow |= pm[hh] > thr[hh];
     }
     if (grow) {
 #pragma unroll
       for (int hh = 0; hh < HB; ++hh) {
-        const float alpha = exp2_fast(m_run[hh] - mnew[hh]);
-        l_run[hh] *= alpha;
-        l_rnd[hh] *= alpha;
-        corr[hh] *= alpha;
+        if (pm[hh] > thr[hh]) {
+          const float alpha = m_run[hh] == -INFINITY ? 0.f : exp2_fast((m_run[hh] - pm[hh]) * kh[hh]);
+          l_run[hh] *= alpha;
+          corr[hh] *= alpha;
 #pragma unroll
-        for (int i = 0; i < CH; ++i) acc[hh][i] *= alpha;
-        m_run[hh] = mnew[hh];
+          for (int i = 0; i < CH; ++i) acc[hh][i] *= alpha;
+          m_run[hh] = pm[hh];
+          thr[hh] = pm[hh] + grow_by[hh];
+          nmk[hh] = -pm[hh] * kh[hh];
+        }
       }
     }
-    const bf16x2 ones = as_bf16x2(0x3f803f80u);
 #pragma unroll
     for (int pp = 0; pp < PP; ++pp) {
-      // channel c of the two tokens as one bf16 pair (byte + 128 of token 0, token 1)
+      // channel c of the two tokens as one bf16 pair (byte + 128 of token 0, token 1):
+      // the fp32 conversion of a byte is exact in its upper half, which one byte
+      // permute per pair moves into place
       uint32_t vp[CH];
 #pragma unroll
       for (int e = 0; e < NW; ++e) {
         const uint32_t x0 = vc[pp][0][e] ^ 0x80808080u, x1 = vc[pp][1][e] ^ 0x80808080u;
 #pragma unroll
         for (int k = 0; k < 4; ++k)
-          vp[4 * e + k] = pack_bf16x2((float)((x0 >> (8 * k)) & 0xffu), (float)((x1 >> (8 * k)) & 0xffu));
+          vp[4 * e + k] = __builtin_amdgcn_perm(__float_as_uint((float)((x1 >> (8 * k)) & 0xffu)),
+                                                __float_as_uint((float)((x0 >> (8 * k)) & 0xffu)), 0x07060302u);
       }
       const bool v0 = (p + pp) * kPage + 2 * tg < n && p + pp < p_end;
       const bool v1 = (p + pp) * kPage + 2 * tg + 1 < n && p + pp < p_end;
+      // invalid tokens (possibly NaN scales) contribute exactly nothing
+      const float s0 = v0 ? vsc[pp][0] : 0.f, s1 = v1 ? vsc[pp][1] : 0.f;
 #pragma unroll
       for (int hh = 0; hh < HB; ++hh) {
-        const float p0 = v0 ? exp2_fast(sc[pp][0][hh] - m_run[hh]) : 0.f;
-        const float p1 = v1 ? exp2_fast(sc[pp][1][hh] - m_run[hh]) : 0.f;
+        const float p0 = v0 ? exp2_fast(fmaf(sc[pp][0][hh], kh[hh], nmk[hh])) : 0.f;
+        const float p1 = v1 ? exp2_fast(fmaf(sc[pp][1][hh], kh[hh], nmk[hh])) : 0.f;
         l_run[hh] += p0 + p1;
-        // the probabilities enter P V as bf16 pairs; O is later divided by the sum of
-        // those rounded values (L uses the fp32 sum).  Invalid tokens (possibly NaN
-        // scales) contribute exactly nothing.
-        const uint32_t pr = pack_bf16x2(p0, p1);
-        l_rnd[hh] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(pr), ones, l_rnd[hh], false);
-        const float s0 = v0 ? vsc[pp][0] : 0.f, s1 = v1 ? vsc[pp][1] : 0.f;
-        const uint32_t ps = pack_bf16x2(bf16lo_to_f32(pr) * s0, bf16hi_to_f32(pr) * s1);
+        const uint32_t ps = pack_bf16x2(p0 * s0, p1 * s1);
         corr[hh] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(ps), as_bf16x2(0x43004300u), corr[hh], false);
 #pragma unroll
         for (int i = 0; i < CH; ++i)
@@ -577,13 +598,16 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_int8_kernel(
     p += kStride;
   }
 
-  // remove the byte offset, combine the 8 token-pair lanes, then the 4 waves
+  // bring the 8 token-pair lanes to a common max, remove the byte offset, combine the
+  // lanes, then the 4 waves (in log2 units)
 #pragma unroll
   for (int hh = 0; hh < HB; ++hh) {
-    l_run[hh] = sum_stride8(l_run[hh]);
-    l_rnd[hh] = sum_stride8(l_rnd[hh]);
+    const float mw = max_stride8(m_run[hh]);
+    const float f = m_run[hh] == -INFINITY ? 0.f : exp2_fast((m_run[hh] - mw) * kh[hh]);
+    l_run[hh] = sum_stride8(l_run[hh] * f);
 #pragma unroll
-    for (int i = 0; i < CH; ++i) acc[hh][i] = sum_stride8(acc[hh][i] - corr[hh]);
+    for (int i = 0; i < CH; ++i) acc[hh][i] = sum_stride8((acc[hh][i] - corr[hh]) * f);
+    m_run[hh] = mw == -INFINITY ? -INFINITY : mw * kh[hh];
   }
   if (lane < 8) {
 #pragma unroll
@@ -591,7 +615,6 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_int8_kernel(
       if (lane == 0) {
         sm_m[w][hh] = m_run[hh];
         sm_l[w][hh] = l_run[hh];
-        sm_lr[w][hh] = l_rnd[hh];
       }
 #pragma unroll
       for (int i = 0; i < CH; ++i) sm_acc[w][hh][dg * CH + i] = acc[hh][i];
@@ -605,17 +628,16 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_int8_kernel(
     float M = -INFINITY;
 #pragma unroll
     for (int ww = 0; ww < kDecWaves; ++ww) M = fmaxf(M, sm_m[ww][hh]);
-    float wsum = 0.f, rsum = 0.f, o = 0.f;
+    float wsum = 0.f, o = 0.f;
 #pragma unroll
     for (int ww = 0; ww < kDecWaves; ++ww) {
       const float mw = sm_m[ww][hh];
       const float f = (mw == -INFINITY) ? 0.f : exp2_fast(mw - M);
       wsum += f * sm_l[ww][hh];
-      rsum += f * sm_lr[ww][hh];
       o += f * sm_acc[ww][hh][d];
     }
     const size_t slot = ((size_t)s * Hq + g * G + hl) * max_splits + split;
-    ws_o[slot * D + d] = o / rsum;
+    ws_o[slot * D + d] = o / wsum;
     if (d == 0) ws_l[slot] = M + log2_fast(wsum);
   }
 }
