@@ -50,10 +50,15 @@ SMALL = [
     (1, 2, 1, 513, 64, True, "bf16"),
     (1, 8, 1, 300, 128, True, "bf16"),
     # grids with both XCD-grouped items and a plain-order tail (GQA group 4: 40 blocks;
-    # MQA group 16: 288 blocks)
+    # MQA group 16: 288 blocks, 17 tiles each)
     (1, 8, 2, 1100, 128, True, "bf16"),
     (2, 16, 1, 2100, 64, False, "bf16"),
     (1, 1, 1, 1024, 128, True, "bf16"),
+    # more items than compute units, so the persistent workgroups take several rounds,
+    # and items with an odd tile count (the next item's first tile is copied after the
+    # epilogue instead of during the last tile): 288 items each
+    (1, 96, 8, 576, 128, True, "bf16"),
+    (2, 48, 48, 640, 64, True, "bf16"),
     (1, 1, 1, 256, 64, False, "f32"),
     (1, 2, 1, 130, 128, True, "f32"),
     (2, 2, 2, 65, 64, True, "f32"),
