@@ -12,7 +12,7 @@ flop/clk; HBM3E 8000 GB/s).  `cpu_baseline` times the fp64 CPU oracle on a bound
 sample of the same workload.
 
 Every timed measurement is warmed for at least --settle-ms of load first, the step
-included; the JSON line records the warm-up, per-step mean/median/min, the graphics
+for at least --step-settle-ms; the JSON line records the warm-up, per-step mean/median/min, the graphics
 clock sampled during the run, the software versions, and the errors of the timed
 step's outputs against the fp64 oracle (`numerics`).
 
@@ -87,7 +87,20 @@ class ClockSampler:
             handles = amdsmi.amdsmi_get_processor_handles()
             h = self._match(amdsmi, handles)
             clk = amdsmi.AmdSmiClkType.GFX
-            self._read = lambda: float(amdsmi.amdsmi_get_clock_info(h, clk)["clk"])
+
+            def read():
+                # mean of the per-XCD graphics clocks of the firmware's metrics table,
+                # else the driver's current-clock query
+                try:
+                    v = [float(x) for x in amdsmi.amdsmi_get_gpu_metrics_info(h)["current_gfxclks"]
+                         if isinstance(x, (int, float)) and 0 < x < 10000]
+                    if v:
+                        return sum(v) / len(v)
+                except Exception:
+                    pass
+                return float(amdsmi.amdsmi_get_clock_info(h, clk)["clk"])
+
+            self._read = read
             self._read()
         except Exception as e:  # no amdsmi, no permission, no device: report it, keep measuring
             self.error = f"{type(e).__name__}: {e}"[:200]
@@ -133,8 +146,9 @@ class ClockSampler:
         self._stop.set()
         if self._thread is not None:
             self._thread.join()
-        out = {"source": "amdsmi_get_clock_info(GFX) current clock, sampled every "
-                         f"{self.period * 1e3:.0f} ms on a host thread"}
+        out = {"source": "amdsmi gpu metrics: mean of the per-XCD current graphics clocks, sampled every "
+                         f"{self.period * 1e3:.0f} ms on a host thread; the firmware refreshes the table "
+                         "with a lag of up to about a second, so a phase's readings trail its load"}
         for ph, v in self.samples.items():
             out[ph] = {"min_mhz": min(v), "mean_mhz": round(sum(v) / len(v), 1), "max_mhz": max(v), "samples": len(v)}
         if self.error:
@@ -309,6 +323,9 @@ def main():
     ap.add_argument("--settle-ms", type=float, default=300.0,
                     help="warm-up floor in milliseconds of load before the timed steps (the clock settles "
                          "within tens of milliseconds)")
+    ap.add_argument("--step-settle-ms", type=float, default=1500.0,
+                    help="warm-up floor in milliseconds of load before the timed steps themselves (long "
+                         "enough for the sampled clock readings, which trail the load, to show it)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-row-stride", type=int, default=1,
                     help="oracle baseline on every n-th query row of the prefill (1 = the whole workload)")
@@ -399,7 +416,7 @@ def main():
     # least --warmup steps and at least --settle-ms of load, so the clock has settled.
     clocks = ClockSampler()
     clocks.start("warmup")
-    n_warm, warm_ms = warm(step, args.warmup, ms_min=args.settle_ms)
+    n_warm, warm_ms = warm(step, args.warmup, ms_min=max(args.settle_ms, args.step_settle_ms))
     log(f"warmup {n_warm} steps in {warm_ms:.0f} ms")
 
     K = args.steps
@@ -418,7 +435,7 @@ def main():
         ev[i][2].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    clock_rec = clocks.stop()
+    clocks.mark("side_measurements")  # sampled on through the measurements beside the step
     p_list = [e[0].elapsed_time(e[1]) for e in ev]
     d_list = [e[1].elapsed_time(e[2]) for e in ev]
     p_ms = sum(p_list) / K
@@ -606,15 +623,18 @@ def main():
             log(f"{name} {o_ms * 1e3:.1f} us ({otf:.1f} TFLOP/s)")
             oc[name] = {"ms": round(o_ms, 5), "TFLOP/s": round(otf, 2), "peak": peak,
                         "frac": round(otf / peak, 4), "algorithmic_flops_per_launch": ofl,
-                        "kernel": ("fwd_f32_kernel" if ocfg.dtype == "f32" else "fwd_bf16_kernel")
+                        "kernel": ("fwd_f32_kernel" if ocfg.dtype == "f32" else "fwd_bf16_persistent_kernel")
                         + f"<{ocfg.d}, {'causal' if ocfg.causal else 'non-causal'}>"}
             del oq, ok_, ov, oo, ol
 
+    clock_rec = clocks.stop()
     res = {"metric": METRIC, "n_gpus": 1, "steps": K, "warmup": args.warmup, "ms_per_step": round(step_ms, 5),
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
            "data": "synthetic (seeded N(0,1) inputs; random page permutation)",
            "timing": {"warmup_steps": n_warm, "warmup_ms": round(warm_ms, 1),
-                      "settle_floor_ms": args.settle_ms, "events": "HIP events on the launch stream"},
+                      "settle_floor_ms": args.settle_ms,
+                      "step_settle_floor_ms": max(args.settle_ms, args.step_settle_ms),
+                      "events": "HIP events on the launch stream"},
            "sclk": clock_rec, "versions": versions()}
     if run_p:
         res["timing"]["prefill"] = stats(p_list)
@@ -629,7 +649,7 @@ def main():
         res.update({"value": round(tf, 2), "unit": "TFLOP/s"})
         res["roofline"] = {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                            "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": tr,
-                           "kernel": "fwd_bf16_kernel<128, causal>", "ms": round(p_ms, 5),
+                           "kernel": "fwd_bf16_persistent_kernel<128, causal>", "ms": round(p_ms, 5),
                            "algorithmic_flops_per_launch": fl}
         cfg_desc["prefill"] = {"B": pcfg.B, "Hq": pcfg.Hq, "Hkv": pcfg.Hkv, "N": pcfg.N, "d": pcfg.d,
                                "causal": pcfg.causal, "seed": pcfg.seed}

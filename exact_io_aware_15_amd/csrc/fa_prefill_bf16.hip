@@ -234,13 +234,12 @@ struct AlibiExt {
 // a wave's diagonal, where steep slopes put almost all of a row's weight on a few
 // keys: the rounding of those few weights to bf16 (2^-9 relative) would otherwise
 // reach O directly, while over many keys the roundings average out.
-template <int D, bool MASK, bool EXT, bool LIN = false, bool RTMASK = false>
+template <int D, bool MASK, bool EXT, bool LIN = false, bool RTMASK = false, bool SPLIT = false>
 __device__ __forceinline__ void process_tile(WaveState<D>& st, const uint8_t* __restrict__ kb,
                                              const uint8_t* __restrict__ vb,
                                              const int (&koff)[D / 16], const int (&voff)[D / 32], int lim,
                                              int l32, float c, int lo = 0, float base = 0.f, float slope2 = 0.f,
-                                             const AlibiExt* ax = nullptr, bool need_mask = false,
-                                             bool split = false) {
+                                             const AlibiExt* ax = nullptr, bool need_mask = false) {
   using LY = Lay<D>;
   constexpr int KK = D / 16;
   constexpr int DB = D / 32;
@@ -314,7 +313,7 @@ __device__ __forceinline__ void process_tile(WaveState<D>& st, const uint8_t* __
         for (int r = 0; r < 16; ++r) sc[a][r] -= sh;
     }
     softmax_pack<D, true, true>(sc, st, 1.f, pb);
-    if (split) {
+    if constexpr (SPLIT) {
       // the second bf16 part of each probability (p = exp2(y), as in softmax_pack)
       const bf16x2 ones = as_bf16x2(0x3f803f80u);
       float rlo = 0.f;
@@ -383,7 +382,7 @@ __device__ __forceinline__ void process_tile(WaveState<D>& st, const uint8_t* __
   __builtin_amdgcn_sched_group_barrier(0x008, kPrefetch, 1);
   debug_read_fence();
   if constexpr (EXT && LIN) {
-    if (split) {
+    if constexpr (SPLIT) {
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int a = 0; a < NA; ++a)
@@ -675,12 +674,22 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void fwd_bf16_kernel(
           // left of it, in the diagonal-first order) carry P in two bf16 parts
           const bool split = rev && ndone < 2;
           ++ndone;
-          if (need_mask)
-            process_tile<D, true, true, CAUSAL>(st, kb, vb, koff, voff, lim, l32, c, lo, base, slope2, &ax, false,
-                                                split);
-          else
-            process_tile<D, false, true, CAUSAL>(st, kb, vb, koff, voff, lim, l32, c, lo, base, slope2, &ax, false,
-                                                 split);
+          // the two-part tiles are instantiations of their own, so the other tiles carry
+          // no code or registers for the second part
+          if (CAUSAL && split) {
+            if constexpr (CAUSAL) {
+              if (need_mask)
+                process_tile<D, true, true, true, false, true>(st, kb, vb, koff, voff, lim, l32, c, lo, base, slope2,
+                                                               &ax);
+              else
+                process_tile<D, false, true, true, false, true>(st, kb, vb, koff, voff, lim, l32, c, lo, base,
+                                                                slope2, &ax);
+            }
+          } else if (need_mask) {
+            process_tile<D, true, true, CAUSAL>(st, kb, vb, koff, voff, lim, l32, c, lo, base, slope2, &ax);
+          } else {
+            process_tile<D, false, true, CAUSAL>(st, kb, vb, koff, voff, lim, l32, c, lo, base, slope2, &ax);
+          }
         } else {
           if constexpr (!CAUSAL) {
             // only a ragged last tile is masked
