@@ -386,11 +386,14 @@ struct ItemSrc {
   int w, lane;
 };
 
-// (query head, row tile) of item i
+// (query head, row tile) of item i.  The unmasked tiles of a head are taken from the
+// last one down: every key block of the head then streams the same Q/dO rows at about
+// the same time (a causal block's first rows are its own, its last ones everybody's),
+// so the blocks of a head that run together on an XCD share them through its L2.
 __device__ __forceinline__ void item_pos(const ItemSrc& s, int item, int& h, int& t) {
   if (item < s.n_un) {
     h = item / s.nu;
-    t = s.t_first + s.n_lead + item % s.nu;
+    t = s.t_first + s.n_lead + (s.nu - 1 - item % s.nu);
   } else {
     const int j = item - s.n_un;
     h = j / s.nm;
