@@ -333,7 +333,8 @@ def main():
                     help="oracle backward baseline on the first n query heads of batch 0")
     ap.add_argument("--cpu-decode-seqs", type=int, default=64,
                     help="oracle baseline on the first n sequences of the decode (64 = the whole workload)")
-    ap.add_argument("--only", choices=["prefill", "decode", "backward", "window", "chunked", "int8", "configs"],
+    ap.add_argument("--only", choices=["prefill", "decode", "backward", "window", "chunked", "int8", "configs",
+                                       "shard"],
                     default=None,
                     help="time one part only (for profiling runs)")
     ap.add_argument("--no-int8", action="store_true",
@@ -344,6 +345,8 @@ def main():
                     help="skip the sliding-window + ALiBi measurement (reported beside the step)")
     ap.add_argument("--no-configs", action="store_true",
                     help="skip timing the forward on the other prefill configurations (reported beside the step)")
+    ap.add_argument("--no-shard", action="store_true",
+                    help="skip timing one GPU's share of the step split over 8 GPUs by heads")
     ap.add_argument("--no-bwd", action="store_true",
                     help="skip the backward measurement (reported beside the step, not part of it)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -383,6 +386,7 @@ def main():
     run_c = args.only == "chunked" or (args.only is None and not args.no_chunked)
     run_i = args.only == "int8" or (args.only is None and not args.no_int8)
     run_o = args.only == "configs" or (args.only is None and not args.no_configs)
+    run_s = args.only == "shard" or (args.only is None and not args.no_shard)
 
     log("generating inputs")
     px = make_inputs(pcfg) if run_p else None
@@ -627,6 +631,58 @@ def main():
                         + f"<{ocfg.d}, {'causal' if ocfg.causal else 'non-causal'}>"}
             del oq, ok_, ov, oo, ol
 
+    sh = None
+    if run_s:
+        # one GPU's share of the step when it is split over 8 GPUs by heads (the shares are
+        # independent, so no collective is involved): the forward with 4 of its 32 heads, the
+        # decode with 1 of its 8 K/V heads and its 4 query heads, same seeds and distributions
+        import dataclasses
+
+        from exact_io_aware_15_amd.workloads import make_decode
+
+        scfg = dataclasses.replace(pcfg, name="c3 share (4 of 32 heads)", Hq=pcfg.Hq // 8, Hkv=pcfg.Hkv // 8)
+        sdcfg = dataclasses.replace(dcfg, name="c5 share (1 of 8 K/V heads)", Hq=dcfg.Hq // 8, Hkv=dcfg.Hkv // 8)
+        sx = make_inputs(scfg)
+        sq, sk, sv = (sx[n].to(dev) for n in "qkv")
+        so, sl = torch.empty_like(sq), torch.empty(sq.shape[:3], dtype=torch.float32, device=dev)
+        sdx = make_decode(sdcfg.num_seqs, sdcfg.Hq, sdcfg.Hkv, sdcfg.d, sdcfg.ctx_lo, sdcfg.ctx_hi, sdcfg.seed,
+                          sdcfg.page_size, sdcfg.max_pages_per_seq, sdcfg.fixed_ctx)
+        sdq, skp, svp = sdx["q"].to(dev), sdx["kpages"].to(dev), sdx["vpages"].to(dev)
+        spt, scl = sdx["page_table"].to(dev), sdx["ctx_lens"].to(dev)
+        sdo, sdl = torch.empty_like(sdq), torch.empty(sdq.shape[:2], dtype=torch.float32, device=dev)
+        sws = torch.empty(fa.fa_decode_paged_workspace_size(sdcfg.num_seqs, sdcfg.Hq, sdcfg.d,
+                                                            sdx["max_pages_per_seq"]), dtype=torch.uint8, device=dev)
+
+        def share_prefill():
+            fa.fa_fwd(sq, sk, sv, causal=scfg.causal, scale=scfg.scale, out=so, lse=sl)
+
+        def share_decode():
+            fa.fa_decode_paged(sdq, skp, svp, spt, scl, scale=sdcfg.scale, out=sdo, lse=sdl, workspace=sws)
+
+        def timed(fn):
+            warm(fn, max(1, args.warmup // 3), ms_min=args.settle_ms)
+            ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
+            for i in range(K):
+                ev[i][0].record()
+                fn()
+                ev[i][1].record()
+            torch.cuda.synchronize()
+            return sum(e[0].elapsed_time(e[1]) for e in ev) / K
+
+        sp_ms, sd_ms = timed(share_prefill), timed(share_decode)
+        sfl = prefill_flops(scfg)
+        sby = decode_bytes(sdx, sdcfg)
+        stf, sgb = sfl / (sp_ms * 1e-3) / 1e12, sby / (sd_ms * 1e-3) / 1e9
+        log(f"share: prefill {sp_ms * 1e3:.1f} us ({stf:.1f} TFLOP/s), decode {sd_ms * 1e3:.1f} us ({sgb:.1f} GB/s)")
+        sh = {"note": "one GPU's share of the step split over 8 GPUs by heads; no collective needed",
+              "prefill": {"workload": f"causal bf16 B{scfg.B} Hq{scfg.Hq} Hkv{scfg.Hkv} N{scfg.N} d{scfg.d}",
+                          "ms": round(sp_ms, 5), "TFLOP/s": round(stf, 2), "frac": round(stf / PEAK_BF16_TFLOPS, 4),
+                          "implied_8gpu_TFLOP/s": round(8 * stf, 1)},
+              "decode": {"workload": f"paged decode {sdcfg.num_seqs} seqs Hq{sdcfg.Hq} Hkv{sdcfg.Hkv} d{sdcfg.d}",
+                         "ms": round(sd_ms, 5), "GB/s": round(sgb, 1), "frac": round(sgb / PEAK_HBM_GBS, 4),
+                         "implied_8gpu_GB/s": round(8 * sgb, 1)}}
+        del sq, sk, sv, so, sl, sdq, skp, svp, spt, scl, sdo, sdl, sws
+
     clock_rec = clocks.stop()
     res = {"metric": METRIC, "n_gpus": 1, "steps": K, "warmup": args.warmup, "ms_per_step": round(step_ms, 5),
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
@@ -677,6 +733,8 @@ def main():
         res["backward"] = bwd
     if oc is not None:
         res["other_configs"] = oc
+    if sh is not None:
+        res["shard_share"] = sh
     if "value" not in res:  # one of the measurements beside the step was run alone
         one = next((x for x in (bwd, wa, cp, d8) if x is not None), None)
         if one is not None:
