@@ -653,8 +653,14 @@ def main():
         sws = torch.empty(fa.fa_decode_paged_workspace_size(sdcfg.num_seqs, sdcfg.Hq, sdcfg.d,
                                                             sdx["max_pages_per_seq"]), dtype=torch.uint8, device=dev)
 
+        sws_p = torch.empty(max(1, fa.fa_fwd_splitk_workspace_size(scfg.B, scfg.Hq, scfg.N, scfg.d, scfg.causal)),
+                            dtype=torch.uint8, device=dev)
+
         def share_prefill():
             fa.fa_fwd(sq, sk, sv, causal=scfg.causal, scale=scfg.scale, out=so, lse=sl)
+
+        def share_prefill_splitk():
+            fa.fa_fwd_splitk(sq, sk, sv, causal=scfg.causal, scale=scfg.scale, out=so, lse=sl, workspace=sws_p)
 
         def share_decode():
             fa.fa_decode_paged(sdq, skp, svp, spt, scl, scale=sdcfg.scale, out=sdo, lse=sdl, workspace=sws)
@@ -669,19 +675,23 @@ def main():
             torch.cuda.synchronize()
             return sum(e[0].elapsed_time(e[1]) for e in ev) / K
 
-        sp_ms, sd_ms = timed(share_prefill), timed(share_decode)
+        sp_ms, sk_ms, sd_ms = timed(share_prefill), timed(share_prefill_splitk), timed(share_decode)
         sfl = prefill_flops(scfg)
         sby = decode_bytes(sdx, sdcfg)
-        stf, sgb = sfl / (sp_ms * 1e-3) / 1e12, sby / (sd_ms * 1e-3) / 1e9
-        log(f"share: prefill {sp_ms * 1e3:.1f} us ({stf:.1f} TFLOP/s), decode {sd_ms * 1e3:.1f} us ({sgb:.1f} GB/s)")
+        stf, skf, sgb = sfl / (sp_ms * 1e-3) / 1e12, sfl / (sk_ms * 1e-3) / 1e12, sby / (sd_ms * 1e-3) / 1e9
+        log(f"share: prefill {sp_ms * 1e3:.1f} us ({stf:.1f} TFLOP/s), split-K {sk_ms * 1e3:.1f} us "
+            f"({skf:.1f} TFLOP/s), decode {sd_ms * 1e3:.1f} us ({sgb:.1f} GB/s)")
         sh = {"note": "one GPU's share of the step split over 8 GPUs by heads; no collective needed",
               "prefill": {"workload": f"causal bf16 B{scfg.B} Hq{scfg.Hq} Hkv{scfg.Hkv} N{scfg.N} d{scfg.d}",
-                          "ms": round(sp_ms, 5), "TFLOP/s": round(stf, 2), "frac": round(stf / PEAK_BF16_TFLOPS, 4),
-                          "implied_8gpu_TFLOP/s": round(8 * stf, 1)},
+                          "fa_fwd": {"ms": round(sp_ms, 5), "TFLOP/s": round(stf, 2),
+                                     "frac": round(stf / PEAK_BF16_TFLOPS, 4)},
+                          "fa_fwd_splitk": {"ms": round(sk_ms, 5), "TFLOP/s": round(skf, 2),
+                                            "frac": round(skf / PEAK_BF16_TFLOPS, 4)},
+                          "implied_8gpu_TFLOP/s": round(8 * max(stf, skf), 1)},
               "decode": {"workload": f"paged decode {sdcfg.num_seqs} seqs Hq{sdcfg.Hq} Hkv{sdcfg.Hkv} d{sdcfg.d}",
                          "ms": round(sd_ms, 5), "GB/s": round(sgb, 1), "frac": round(sgb / PEAK_HBM_GBS, 4),
                          "implied_8gpu_GB/s": round(8 * sgb, 1)}}
-        del sq, sk, sv, so, sl, sdq, skp, svp, spt, scl, sdo, sdl, sws
+        del sq, sk, sv, so, sl, sdq, skp, svp, spt, scl, sdo, sdl, sws, sws_p
 
     clock_rec = clocks.stop()
     res = {"metric": METRIC, "n_gpus": 1, "steps": K, "warmup": args.warmup, "ms_per_step": round(step_ms, 5),

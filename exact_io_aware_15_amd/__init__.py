@@ -25,6 +25,8 @@ __all__ = [
     "fa_fwd",
     "fa_fwd_f32",
     "fa_fwd_ex",
+    "fa_fwd_splitk",
+    "fa_fwd_splitk_workspace_size",
     "fa_bwd",
     "fa_bwd_workspace_size",
     "fa_decode_paged",
@@ -94,6 +96,10 @@ def load_library(path: str) -> ctypes.CDLL:
     L.fa_fwd_f32.restype = i
     L.fa_fwd_ex.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp, vp]
     L.fa_fwd_ex.restype = i
+    L.fa_fwd_splitk_workspace_size.argtypes = [i, i, i, i, i]
+    L.fa_fwd_splitk_workspace_size.restype = sz
+    L.fa_fwd_splitk.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp, sz, vp]
+    L.fa_fwd_splitk.restype = i
     L.fa_bwd_workspace_size.argtypes = [i, i, i, i, i]
     L.fa_bwd_workspace_size.restype = sz
     L.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp, sz, vp]
@@ -168,6 +174,40 @@ def _fwd(entry: str, dtype, q, k, v, causal, scale, out, lse):
 def fa_fwd(q, k, v, causal=False, scale=None, out=None, lse=None):
     """bf16 forward: q [B,Hq,N,d], k/v [B,Hkv,N,d] -> (O bf16 [B,Hq,N,d], L fp32 [B,Hq,N])."""
     return _fwd("fa_fwd", torch.bfloat16, q, k, v, causal, scale, out, lse)
+
+
+def fa_fwd_splitk_workspace_size(B, Hq, N, d, causal) -> int:
+    return int(lib().fa_fwd_splitk_workspace_size(B, Hq, N, d, int(bool(causal))))
+
+
+def fa_fwd_splitk(q, k, v, causal=False, scale=None, out=None, lse=None, workspace=None):
+    """fa_fwd with the key range of each query block cut into chunks when the launch has
+    fewer than 256 (query block, head) items; workspace: a uint8 device tensor of at least
+    fa_fwd_splitk_workspace_size(...) bytes (allocated here when None)."""
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q must be [B, Hq, N, d] and k, v [B, Hkv, N, d]")
+    B, Hq, N, d = q.shape
+    Hkv = k.shape[1]
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on a GPU")
+    _need(q, "q", torch.bfloat16, (B, Hq, N, d), dev)
+    _need(k, "k", torch.bfloat16, (B, Hkv, N, d), dev)
+    _need(v, "v", torch.bfloat16, (B, Hkv, N, d), dev)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    out = torch.empty((B, Hq, N, d), dtype=torch.bfloat16, device=dev) if out is None else out
+    lse = torch.empty((B, Hq, N), dtype=torch.float32, device=dev) if lse is None else lse
+    _need(out, "out", torch.bfloat16, (B, Hq, N, d), dev)
+    _need(lse, "lse", torch.float32, (B, Hq, N), dev)
+    if workspace is None:
+        workspace = torch.empty(max(1, fa_fwd_splitk_workspace_size(B, Hq, N, d, causal)), dtype=torch.uint8,
+                                device=dev)
+    st = lib().fa_fwd_splitk(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv, N, d, int(bool(causal)),
+                             float(scale), _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(q))
+    if st != FA_OK:
+        raise FAError(st, "fa_fwd_splitk")
+    return out, lse
 
 
 def fa_fwd_f32(q, k, v, causal=False, scale=None, out=None, lse=None):

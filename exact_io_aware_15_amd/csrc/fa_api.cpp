@@ -97,6 +97,29 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
   return finish(fa::launch_fwd_bf16(a), stream);
 }
 
+size_t fa_fwd_splitk_workspace_size(int B, int Hq, int N, int d, int causal) {
+  if (B < 1 || Hq < 1 || N < 1 || (d != 64 && d != 128) || (causal != 0 && causal != 1)) return 0;
+  return fa::fwd_split_plan(B, Hq, N, d, causal != 0).bytes;
+}
+
+int fa_fwd_splitk(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv, int N,
+                  int d, int causal, float scale, void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_fwd_args(B, Hq, Hkv, N, d, causal, scale);
+  if (st == FA_OK) st = check_fwd_bf16_sizes(B, Hq, N, d);
+  if (st == FA_OK) st = check_fwd_ptrs(q, k, v, o, lse);
+  if (st != FA_OK) return st;
+  const fa::SplitPlan pl = fa::fwd_split_plan(B, Hq, N, d, causal != 0);
+  // the merge grid: one 256-thread workgroup per 1024 / d rows of every (head, query block)
+  if (!fits((long long)B * Hq * pl.nqb * (fa::kGeomFwdRows / (1024 / d)), 256)) return FA_ERR_SHAPE;
+  if (pl.bytes > 0) {
+    if (!workspace || workspace_bytes < pl.bytes) return FA_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return FA_ERR_ALIGN;
+  }
+  fa::FwdArgs a{q, k, v, o, lse, B, Hq, Hkv, N, d, causal != 0, scale, stream};
+  a.workspace = workspace;
+  return finish(fa::launch_fwd_splitk(a), stream);
+}
+
 int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv, int N,
               int d, int causal, float scale, int window, const float* alibi_slopes, void* stream) {
   if (window < 0) return FA_ERR_SHAPE;

@@ -3,6 +3,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <algorithm>
 #include <stddef.h>
 #include <stdint.h>
 
@@ -26,6 +27,7 @@ struct FwdArgs {
   const int32_t* ctx_lens = nullptr;
   int max_pages = 0;
   int num_pages = 0;              // pages in each pool (page ids are clamped below it)
+  void* workspace = nullptr;      // split-K forward (launch_fwd_splitk): fp32 partials
 };
 
 struct DecodeArgs {
@@ -76,6 +78,57 @@ inline size_t decode_workspace_bytes(int S, int Hq, int d, int max_pages) {
   return ((o_bytes + 255) / 256) * 256 + l_bytes;
 }
 
+// Split-K forward plan (fa_fwd_splitk).  When a launch has fewer (256-row query block,
+// head) items than kSplitTargetItems workgroups (256: the MI355X compute units), the
+// key tiles of each block are cut into chunks of T tiles, T the smallest value (at
+// least 4) that keeps the item count within the target; blocks with more than one
+// chunk leave fp32 (O, lse) partials in the workspace for a merge.  Otherwise nothing is
+// split (T = the longest block's tile count) and no workspace is needed.
+// Workspace: O partials [B*Hq][query blocks][smax][256][d] fp32 (padded to 256 B), then
+// per partial row m + log2 of its fp32 probability sum, then m + log2 of the sum of
+// its bf16-rounded probabilities (each [B*Hq][query blocks][smax][256] fp32).
+constexpr int kSplitTargetItems = 256;
+inline int fwd_key_tiles(int N, int d, bool causal, int qb) {
+  const int bc = d == 64 ? 128 : 64;
+  const long long kend = causal ? std::min<long long>(N, (long long)(qb + 1) * kGeomFwdRows) : N;
+  return (int)((kend + bc - 1) / bc);
+}
+struct SplitPlan {
+  int T, smax, nqb;
+  long long items;
+  size_t o_bytes, bytes;
+};
+inline SplitPlan fwd_split_plan(int B, int Hq, int N, int d, bool causal) {
+  SplitPlan p;
+  p.nqb = (N + kGeomFwdRows - 1) / kGeomFwdRows;
+  const long long BH = (long long)B * Hq;
+  const int maxt = fwd_key_tiles(N, d, causal, p.nqb - 1);
+  auto items_for = [&](int T) {
+    long long n = 0;
+    for (int qb = 0; qb < p.nqb; ++qb) n += (fwd_key_tiles(N, d, causal, qb) + T - 1) / T;
+    return n * BH;
+  };
+  p.T = maxt;
+  if (BH * p.nqb < kSplitTargetItems) {
+    for (int T = std::min(4, maxt); T < maxt; ++T)
+      if (items_for(T) <= kSplitTargetItems) {
+        p.T = T;
+        break;
+      }
+  }
+  p.smax = (maxt + p.T - 1) / p.T;
+  p.items = items_for(p.T);
+  if (p.smax > 1) {
+    const size_t rows = (size_t)BH * p.nqb * p.smax * kGeomFwdRows;
+    p.o_bytes = (rows * d * sizeof(float) + 255) / 256 * 256;
+    p.bytes = p.o_bytes + 2 * rows * sizeof(float);
+  } else {
+    p.o_bytes = 0;
+    p.bytes = 0;
+  }
+  return p;
+}
+
 struct BwdArgs {
   const void* q;
   const void* k;
@@ -121,6 +174,7 @@ inline BwdPlan bwd_plan(int B, int Hq, int Hkv, int N, int d) {
 }
 
 hipError_t launch_fwd_bf16(const FwdArgs& a);
+hipError_t launch_fwd_splitk(const FwdArgs& a);
 hipError_t launch_prefill_paged(const FwdArgs& a);
 hipError_t launch_bwd_bf16(const BwdArgs& a);
 hipError_t launch_fwd_f32(const FwdArgs& a);

@@ -472,10 +472,16 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void fwd_bf16_kernel(
     float c /* |scale| * log2(e), > 0 */, uint32_t qsign /* 0x80008000 if scale < 0 */,
     int window /* EXT: keys j >= i - window + 1 only (0: none) */, const float* __restrict__ slopes /* EXT: ALiBi */,
     const int32_t* __restrict__ table /* PAGED */, const int32_t* __restrict__ ctxl /* PAGED */,
-    int max_pages /* PAGED */, int num_pages /* PAGED */) {
+    int max_pages /* PAGED */, int num_pages /* PAGED */, int split_tiles /* split-K: key tiles per chunk */,
+    float* __restrict__ ws_o /* split-K: O partials */, float* __restrict__ ws_l /* split-K: lse partials */,
+    int smax /* split-K: chunk slots per block */, int ws_rows /* split-K: rows of partials */) {
   using LY = Lay<D>;
   constexpr int KK = D / 16;
   constexpr int DB = D / 32;
+  // The plain instantiation (no window, ALiBi or paging) is the split-K forward: each
+  // workgroup takes one chunk of split_tiles key tiles of a (query block, head); a block
+  // cut into several chunks leaves fp32 (O, lse) partials for fwd_split_merge_kernel.
+  constexpr bool SPLIT = !EXT && !PAGED;
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kStages * LY::TBYTES];
 
   const int nqb = (N + kBR - 1) / kBR;
@@ -494,12 +500,27 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void fwd_bf16_kernel(
   // items keeps the plain order.
   const int S = PAGED ? G * nqb : G;
   int item = (int)blockIdx.x;
-  if (item < (int)(gridDim.x / (8 * S)) * 8 * S) {
+  if (!SPLIT && item < (int)(gridDim.x / (8 * S)) * 8 * S) {
     const int x = item & 7, slot = item >> 3, k = slot / S;
     item = (8 * k + ((k & 1) ? 7 - x : x)) * S + slot % S;
   }
   int qb, b, h;
-  if constexpr (PAGED) {
+  int split = 0, nsplit = 1;
+  if constexpr (SPLIT) {
+    // heaviest blocks first (causal); per block its chunks, per chunk the heads
+    const int BH = B * Hq;
+    qb = 0;
+    for (int r = 0; r < nqb; ++r) {
+      qb = CAUSAL ? nqb - 1 - r : r;
+      const int kend_q = CAUSAL ? min(N, (qb + 1) * kBR) : N;
+      nsplit = ((kend_q + LY::BC - 1) / LY::BC + split_tiles - 1) / split_tiles;
+      if (item < nsplit * BH) break;
+      item -= nsplit * BH;
+    }
+    split = item / BH;
+    b = (item % BH) / Hq;
+    h = (item % BH) % Hq;
+  } else if constexpr (PAGED) {
     const int per_seq = Hkv * nqb * G;
     b = item / per_seq;
     const int r = item % per_seq;
@@ -569,9 +590,13 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void fwd_bf16_kernel(
   }
 
   const int kend = CAUSAL ? min(Nk, poff + (qb + 1) * kBR) : Nk;
-  const int ntiles = (kend + LY::BC - 1) / LY::BC;
+  int ntiles = (kend + LY::BC - 1) / LY::BC;
   // sliding window: tiles wholly left of the block's first row's window are never loaded
-  const int t_begin = (EXT && window > 0) ? max(0, poff + qb * kBR - window + 1) / LY::BC : 0;
+  int t_begin = (EXT && window > 0) ? max(0, poff + qb * kBR - window + 1) / LY::BC : 0;
+  if constexpr (SPLIT) {
+    t_begin = split * split_tiles;
+    ntiles = min(ntiles, t_begin + split_tiles);
+  }
   const float slope2 = (EXT && slopes != nullptr) ? slopes[h] * kLog2e : 0.f;
   AlibiExt ax;
   if constexpr (EXT && CAUSAL) {
@@ -712,6 +737,28 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void fwd_bf16_kernel(
   // ---- epilogue: O = O / l_round (bf16), L = (m + log2 l_exact) ln 2
   const float lr = sum_xor32(st.l_round);
   const float le = sum_xor32(st.l_exact);
+  if (SPLIT && nsplit > 1) {
+    // this chunk's partial: O / l_round, m + log2 l_exact and m + log2 l_round (log2 units)
+    // in fp32; a row with no visible key in the chunk leaves O = 0 and -inf
+    const float pinv = lr > 0.f ? 1.f / lr : 0.f;
+    if (qrow < N) {
+      const size_t slot = (((size_t)(b * Hq + h) * nqb + qb) * smax + split) * kBR + (qrow - qb * kBR);
+      float* orow = ws_o + slot * D;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const f32x4 v4 = {st.oacc[db][4 * g4 + 0] * pinv, st.oacc[db][4 * g4 + 1] * pinv,
+                            st.oacc[db][4 * g4 + 2] * pinv, st.oacc[db][4 * g4 + 3] * pinv};
+          *reinterpret_cast<f32x4*>(orow + db * 32 + 8 * g4 + 4 * hi) = v4;
+        }
+      if (hi == 0) {
+        ws_l[slot] = le > 0.f ? st.m_run + log2_fast(le) : -INFINITY;
+        ws_l[(size_t)ws_rows + slot] = lr > 0.f ? st.m_run + log2_fast(lr) : -INFINITY;
+      }
+    }
+    return;
+  }
   const float inv = 1.f / lr;
   if (qrow < N) {
     uint16_t* orow = O + ((size_t)(b * Hq + h) * N + qrow) * D;
@@ -949,7 +996,80 @@ hipError_t launch(const FwdArgs& a) {
   hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, EXT, PAGED>), grid, dim3(kThreads), 0, (hipStream_t)a.stream,
                      (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o,
                      a.lse, a.B, a.Hq, a.Hkv, a.N, c, qsign, a.window, a.slopes, a.page_table, a.ctx_lens,
-                     a.max_pages, a.num_pages);
+                     a.max_pages, a.num_pages, 0, nullptr, nullptr, 1, 0);
+  return hipGetLastError();
+}
+
+// Sum of the chunk partials of the blocks the split-K plan cut (the decode's
+// log-sum-exp merge).  O = sum_c r_c O_c / sum_c r_c with r_c = exp2(lr_c - max lr), lr_c
+// the log2 of chunk c's sum of bf16-rounded probabilities: O_c was normalised by that
+// sum, so this is exactly the one-pass O (the sum of the rounded weights times V, over
+// their sum).  L = (max le + log2 sum_c exp2(le_c - max le)) ln 2 from the fp32 sums.
+// One workgroup per RPP rows of a (head, query block) (RPP = 1024 / d: a thread per four
+// channels of a row); blocks left whole wrote O and L themselves.
+template <int D>
+constexpr int kMergeRows = 1024 / D;
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256) void fwd_split_merge_kernel(const float* __restrict__ ws_o,
+                                                              const float* __restrict__ ws_l, uint16_t* __restrict__ O,
+                                                              float* __restrict__ Lse, int N, int nqb, int split_tiles,
+                                                              int smax, int ws_rows) {
+  const float* __restrict__ ws_r = ws_l + ws_rows;
+  using LY = Lay<D>;
+  constexpr int TPR = D / 4;             // threads per row (four channels each)
+  constexpr int RPP = kMergeRows<D>;     // rows per workgroup
+  constexpr int PPB = kBR / RPP;         // workgroups per query block
+  const int blk = blockIdx.x / PPB, part = blockIdx.x % PPB;
+  const int bh = blk / nqb, qb = blk % nqb;
+  const int kend = CAUSAL ? min(N, (qb + 1) * kBR) : N;
+  const int nsplit = ((kend + LY::BC - 1) / LY::BC + split_tiles - 1) / split_tiles;
+  if (nsplit <= 1) return;
+  const int tid = threadIdx.x, rr = tid / TPR, c4 = (tid % TPR) * 4;
+  const size_t slot0 = ((size_t)bh * nqb + qb) * smax;
+  {
+    const int r = part * RPP + rr, row = qb * kBR + r;
+    if (row >= N) return;
+    float Me = -INFINITY, Mr = -INFINITY;
+    for (int c = 0; c < nsplit; ++c) {
+      Me = fmaxf(Me, ws_l[(slot0 + c) * kBR + r]);
+      Mr = fmaxf(Mr, ws_r[(slot0 + c) * kBR + r]);
+    }
+    float esum = 0.f, rsum = 0.f;
+    f32x4 o = {0.f, 0.f, 0.f, 0.f};
+    for (int c = 0; c < nsplit; ++c) {
+      const float le = ws_l[(slot0 + c) * kBR + r], lr = ws_r[(slot0 + c) * kBR + r];
+      esum += le == -INFINITY ? 0.f : exp2_fast(le - Me);
+      const float wc = lr == -INFINITY ? 0.f : exp2_fast(lr - Mr);
+      rsum += wc;
+      o += wc * *reinterpret_cast<const f32x4*>(ws_o + ((slot0 + c) * kBR + r) * D + c4);
+    }
+    const float inv = rsum > 0.f ? 1.f / rsum : 0.f;
+    u32x2 w2;
+    w2[0] = pack_bf16x2(o[0] * inv, o[1] * inv);
+    w2[1] = pack_bf16x2(o[2] * inv, o[3] * inv);
+    *reinterpret_cast<u32x2*>(O + ((size_t)bh * N + row) * D + c4) = w2;
+    if (c4 == 0) Lse[(size_t)bh * N + row] = esum > 0.f ? (Me + log2_fast(esum)) * kLn2 : -INFINITY;
+  }
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch_split(const FwdArgs& a) {
+  const SplitPlan pl = fwd_split_plan(a.B, a.Hq, a.N, a.d, a.causal);
+  float c = fabsf(a.scale) * kLog2e;
+  if (!(c > 1e-30f)) c = 1e-30f;
+  const uint32_t qsign = a.scale < 0.f ? 0x80008000u : 0u;
+  float* wso = pl.smax > 1 ? (float*)a.workspace : nullptr;
+  float* wsl = pl.smax > 1 ? (float*)((uint8_t*)a.workspace + pl.o_bytes) : nullptr;
+  const int ws_rows = pl.smax > 1 ? a.B * a.Hq * pl.nqb * pl.smax * kBR : 0;
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, false, false>), dim3((unsigned)pl.items), dim3(kThreads), 0,
+                     (hipStream_t)a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
+                     (uint16_t*)a.o, a.lse, a.B, a.Hq, a.Hkv, a.N, c, qsign, 0, nullptr, nullptr, nullptr, 0, 0,
+                     pl.T, wso, wsl, pl.smax, ws_rows);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || pl.smax <= 1) return e;
+  hipLaunchKernelGGL((fwd_split_merge_kernel<D, CAUSAL>),
+                     dim3((unsigned)(a.B * a.Hq * pl.nqb * (kBR / kMergeRows<D>))), dim3(256), 0,
+                     (hipStream_t)a.stream, wso, wsl, (uint16_t*)a.o, a.lse, a.N, pl.nqb, pl.T, pl.smax, ws_rows);
   return hipGetLastError();
 }
 
@@ -982,6 +1102,11 @@ hipError_t launch_persistent(const FwdArgs& a) {
 }
 
 }  // namespace
+
+hipError_t launch_fwd_splitk(const FwdArgs& a) {
+  if (a.d == 64) return a.causal ? launch_split<64, true>(a) : launch_split<64, false>(a);
+  return a.causal ? launch_split<128, true>(a) : launch_split<128, false>(a);
+}
 
 hipError_t launch_prefill_paged(const FwdArgs& a) {
   return a.d == 64 ? launch<64, true, false, true>(a) : launch<128, true, false, true>(a);

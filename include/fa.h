@@ -83,6 +83,37 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
            void* stream);
 
 /*
+ * fa_fwd_splitk_workspace_size -- bytes of device workspace fa_fwd_splitk needs
+ * for these sizes: 0 when the launch has at least 256 (query block of 256 rows,
+ * head) items and nothing is split, else the fp32 partials (O and logsumexp) of
+ * the blocks whose key range is cut into chunks.  Returns 0 when an argument is
+ * out of range.
+ */
+size_t fa_fwd_splitk_workspace_size(int B, int Hq, int N, int d, int causal);
+
+/*
+ * fa_fwd_splitk -- fa_fwd for launches with few heads (one GPU's share of a
+ * head-sharded model, short batches): the same operation, tensors, outputs and
+ * status codes, with the key range of each query block cut into chunks when the
+ * launch has fewer than 256 (query block, head) items, so the chunks spread over
+ * all the compute units instead of the heaviest causal block setting the time.
+ *
+ * Pages: as fa_fwd; the chunks' partial (O, logsumexp) are combined by the
+ * log-sum-exp merge of the split-K decode ("Phase 08", Lab 03 step 4: split-K
+ * over the keys), which gives the same exact attention.
+ *
+ *   workspace: device memory of at least fa_fwd_splitk_workspace_size(B, Hq, N,
+ *   d, causal) bytes, 16-byte aligned, owned by the caller (may be NULL when that
+ *   size is 0); contents on entry do not matter.  Calls sharing a workspace must
+ *   be ordered (same stream).
+ * Returns FA_OK or a status code above (FA_ERR_WORKSPACE for a missing or short
+ * workspace).
+ */
+int fa_fwd_splitk(const void* q, const void* k, const void* v, void* o, float* lse,
+                  int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+                  void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * fa_fwd_f32 -- the same operation in fp32 throughout (inputs, the P V product
  * with unrounded fp32 probabilities, accumulation and O).  Same pages, same
  * parameter list and layouts as fa_fwd with every tensor fp32.

@@ -95,3 +95,62 @@ def check_bf16(O, L, Oref, Lref, what, tol_o=1e-2, tol_l=1e-3):
 
 def check_f32(O, L, Oref, Lref, what, tol_o=1e-4, tol_l=1e-4):
     return check_outputs(O, L, Oref, Lref, what, tol_o, tol_l, False)
+
+
+# ---- per-element bound of the bf16 forward's own roundings -------------------------
+# The kernels give the P V product bf16-rounded probabilities r_j = p_j (1 + e_j),
+# |e_j| <= 2^-8, and divide by their sum, so with w_j = p_j / sum p:
+#   O_fp32 - O = sum_j w_j e_j (v_j - O) / (1 + sum_j w_j e_j),
+# at most 2^-8 sum_j w_j |v_j - O| / (1 - 2^-8); the fp32 sums over n keys add up to
+# n 2^-24 sum_j w_j |v_j|, and rounding O_fp32 to bf16 half a bf16 ulp.  On rows where
+# a few keys carry the weight (scales far above 1/sqrt(d)) the first term no longer
+# averages out and, with the output rounding, can exceed the 1e-2 bar where |O| lies in
+# [2, 4) and the bf16 floor rule does not apply.
+U_P = 2.0 ** -8
+SLACK_P = 1.5   # exp2 and the scores' fp32 sums perturb p by well under 2^-9 relative
+
+
+def fwd_p_bound(q, k, v, Oref, Lref, causal, scale, rows_per_chunk=16):
+    """Per-element bound on |O_gpu - O| of the bf16 forward; q [B,Hq,N,d], k/v [B,Hkv,N,d]
+    fp64 numpy, Oref/Lref the oracle's outputs."""
+    B, Hq, N, d = q.shape
+    G = Hq // k.shape[1]
+    dev = np.zeros_like(Oref)
+    acc = np.zeros_like(Oref)
+    keys = np.arange(N)
+    for b in range(B):
+        for h in range(Hq):
+            K, V = k[b, h // G], v[b, h // G]
+            for r0 in range(0, N, rows_per_chunk):
+                rows = np.arange(r0, min(N, r0 + rows_per_chunk))
+                s = scale * (q[b, h, rows] @ K.T)
+                if causal:
+                    s = np.where(keys[None, :] <= rows[:, None], s, -np.inf)
+                w = np.exp(s - Lref[b, h, rows][:, None])               # softmax weights
+                o = Oref[b, h, rows]
+                dev[b, h, rows] = np.einsum("rj,rjc->rc", w, np.abs(V[None, :, :] - o[:, None, :]))
+                acc[b, h, rows] = w @ np.abs(V)
+    e32 = SLACK_P * (U_P / (1 - U_P) * dev + N * 2.0 ** -24 * acc)
+    _, _, sp = bf16_bracket(np.abs(Oref) + e32 + 1e-300)
+    return e32 + sp / 2
+
+
+def check_bf16_p_bound(O, L, Oref, Lref, bound, what, tol_o=1e-2, tol_l=1e-3):
+    """The bf16 check with one more allowance: an element above the bar passes when it
+    lies within the forward's own per-element rounding bound (fwd_p_bound)."""
+    O, L = f64(O), f64(L)
+    err = np.abs(O - Oref)
+    over = err > tol_o
+    bad = over & (err > bound)
+    fin = np.isfinite(Lref)
+    el = float(np.abs(L[fin] - Lref[fin]).max()) if fin.any() else 0.0
+    ratio = float((err / bound).max()) if err.size else 0.0
+    say(f"{what}: max|dO|={err.max():.3e}, {int(over.sum())} elements above {tol_o:g}, largest error over "
+        f"the P-rounding bound {ratio:.2f}, max|dL|={el:.3e}")
+    if bad.any():
+        idx = np.argwhere(bad)[:4].tolist()
+        raise AssertionError(f"{what}: O error above both the bar and the rounding bound at {idx}: "
+                             f"gpu {O[bad][:4].tolist()} ref {Oref[bad][:4].tolist()} bound {bound[bad][:4].tolist()}")
+    assert np.all(np.isfinite(O)), f"{what}: non-finite O"
+    assert el <= tol_l, f"{what}: L error {el} > {tol_l}"
+    return ratio

@@ -253,3 +253,36 @@ def test_decode_noalloc_validation(L):
         maxp += 128
     assert na(L, S=S, Hq=Hq, Hkv=8, d=d, maxp=maxp) == SCRATCH
     assert "scratch" in fa.fa_status_string(SCRATCH)
+
+
+def splitk(L, q=P, k=P, v=P, o=P, lse=P, B=1, Hq=4, Hkv=4, N=8192, d=128, causal=1, scale=0.088, ws=P,
+           ws_bytes=1 << 40):
+    return L.fa_fwd_splitk(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, scale, ws, ws_bytes, Z)
+
+
+def test_fwd_splitk_workspace_size(L):
+    # a launch with at least 256 (256-row query block, head) items is not split
+    assert fa.fa_fwd_splitk_workspace_size(1, 32, 8192, 128, 1) == 0
+    assert fa.fa_fwd_splitk_workspace_size(4, 16, 2048, 64, 0) == 0
+    # one GPU's share of the c3 forward (4 heads: 128 items) is, in fp32 partials of
+    # 256 rows x (d + 1) per chunk slot
+    sz = fa.fa_fwd_splitk_workspace_size(1, 4, 8192, 128, 1)
+    assert sz >= 2 * 4 * 32 * 256 * (128 + 1) * 4
+    # out-of-range arguments
+    for args in [(0, 4, 8192, 128, 1), (1, 0, 8192, 128, 1), (1, 4, 0, 128, 1), (1, 4, 8192, 96, 1),
+                 (1, 4, 8192, 128, 2)]:
+        assert L.fa_fwd_splitk_workspace_size(*args) == 0
+
+
+def test_fwd_splitk_validation(L):
+    need = fa.fa_fwd_splitk_workspace_size(1, 4, 8192, 128, 1)
+    assert splitk(L, q=Z) == NULL
+    assert splitk(L, d=96) == UNSUP
+    assert splitk(L, Hq=3, Hkv=2) == SHAPE
+    assert splitk(L, N=0) == SHAPE
+    assert splitk(L, scale=float("nan")) == SCALE
+    assert splitk(L, v=MIS) == ALIGN
+    # a split launch needs its workspace: missing, short or misaligned
+    assert splitk(L, ws=Z) == WORKSPACE
+    assert splitk(L, ws_bytes=need - 1) == WORKSPACE
+    assert splitk(L, ws=MIS, ws_bytes=need) == ALIGN
