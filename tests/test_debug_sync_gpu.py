@@ -69,3 +69,12 @@ def test_backward_fast_equals_debug_sync(name):
     do = make_grad_output(cfg.B, cfg.Hq, cfg.N, cfg.d, seed=cfg.seed).to(DEV)
     o, l = fa.fa_fwd(q, k, v, causal=cfg.causal, scale=cfg.scale)
     same(*both(lambda: fa.fa_bwd(q, k, v, o, l, do, causal=cfg.causal, scale=cfg.scale)), f"fa_bwd {name}")
+
+
+def test_fwd_splitk_fast_equals_debug_sync():
+    """The 4-head share of the causal N8192 forward, whose key tiles the split-K path cuts
+    into chunks; the chunk partials and their merge both compared."""
+    cfg = CONFIGS["c3_bf16_causal_B1_H32_N8192_d128"]
+    x = make_inputs(cfg)
+    q, k, v = (x[n][:, :4].contiguous().to(DEV) for n in "qkv")
+    same(*both(lambda: fa.fa_fwd_splitk(q, k, v, causal=True, scale=cfg.scale)), "fa_fwd_splitk c3 4 heads")
