@@ -31,6 +31,7 @@
 #include "fa_device.h"
 #include "fa_launch.h"
 
+
 namespace fa {
 namespace {
 
@@ -339,16 +340,17 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
 // INT8 group-scaled KV cache (screna.ai KV-cache quantization block: 8-bit cache
 // with group-wise scales).  K/V pages hold int8 values, one fp32 scale per
 // (page, K/V head, token, 32 consecutive channels); the value is int8 * scale.
-// Same grid, page-id register and ping-pong buffers as decode_split_kernel; lane
-// l holds tokens 2(l/8), 2(l/8)+1 and channels (l%8)*CH .. +CH (one 32-channel
-// group), CH = D/8.  The offsets are removed algebraically.
+// Same grid, page-id register and ping-pong buffers as decode_split_kernel, one page
+// per wave iteration; lane l holds tokens 2(l/8), 2(l/8)+1 and channels
+// (l%8)*CH .. +CH (one 32-channel group), CH = D/8.
 //  - Keys: byte b enters as the fp16 value 1024 + (b + 128), built by one byte permute per channel pair (b ^ 0x80 as the
 //    low byte under a 0x64 high byte), against q converted exactly to fp16 under a power-of-two scale per head.  Then
-//    q.k = sum q_c (1152 + b_c) - 1152 sum q_c, with fp16 pair dot products and fp32 sums (the products are exact).
-//  - Values: byte b enters as the bf16 value b + 128 (exact for 1 .. 255: the fp32 conversion's upper half), so
-//    O += p s (b + 128) - 128 p s per group, with bf16 pair dot products.  p s enters P V rounded to bf16; O and L are
-//    normalised by the fp32 sum of the probabilities.  (fp16 would bound p s to its range, which arbitrary scales need
-//    not respect.)
+//    q.k = sum q_c (1152 + b_c) - 1152 sum q_c, with fp16 pair dot products and fp32 sums (the products are exact): the
+//    key offset is removed algebraically.
+//  - Values: the signed byte b enters as the bf16 value b (at most 8 significant bits: the upper half of its fp32
+//    conversion, one sign-extending instruction), so O += (p s) b per group with bf16 pair dot products and exact
+//    products.  p s enters P V rounded to bf16; O and L are normalised by the fp32 sum of the probabilities.  (fp16
+//    would bound p s to its range, which arbitrary scales need not respect.)
 //  - Softmax: each lane keeps its own running maximum of the raw scores q.k * kscale (the factor k = |scale| log2(e)
 //    times the head's q unscale enters the exponent's fused multiply-add), raised only when a score passes it by more
 //    than 8 / k, so probabilities stay at most 2^8 and no per-page reduction across lanes is needed.  The lanes'
@@ -380,7 +382,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_int8_kernel(
   constexpr int CH = D / 8;           // channels per lane
   constexpr int NG = D / 32;          // scale groups per token
   constexpr int NW = CH / 4;          // 32-bit words per token per lane
-  constexpr int PP = 2;               // pages consumed per wave iteration
+  constexpr int PP = 1;               // pages consumed per wave iteration
   constexpr float kGrow = 8.f;        // log2 units a score may exceed the running max by
   typedef typename I8Vec<CH>::T vec_t;
   __shared__ float sm_m[kDecWaves][HB];
@@ -453,14 +455,13 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_int8_kernel(
 
   // per lane: running max of the raw scores, the score that triggers a rescale, -max*k,
   // the fp32 probability sum, the offset correction and the unnormalised output
-  float m_run[HB], thr[HB], nmk[HB], l_run[HB], corr[HB], acc[HB][CH];
+  float m_run[HB], thr[HB], nmk[HB], l_run[HB], acc[HB][CH];
 #pragma unroll
   for (int hh = 0; hh < HB; ++hh) {
     m_run[hh] = -INFINITY;
     thr[hh] = -INFINITY;
     nmk[hh] = 0.f;
     l_run[hh] = 0.f;
-    corr[hh] = 0.f;
 #pragma unroll
     for (int i = 0; i < CH; ++i) acc[hh][i] = 0.f;
   }
@@ -544,7 +545,6 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_int8_kernel(
         if (pm[hh] > thr[hh]) {
           const float alpha = m_run[hh] == -INFINITY ? 0.f : exp2_fast((m_run[hh] - pm[hh]) * kh[hh]);
           l_run[hh] *= alpha;
-          corr[hh] *= alpha;
 #pragma unroll
           for (int i = 0; i < CH; ++i) acc[hh][i] *= alpha;
           m_run[hh] = pm[hh];
@@ -555,17 +555,17 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_int8_kernel(
     }
 #pragma unroll
     for (int pp = 0; pp < PP; ++pp) {
-      // channel c of the two tokens as one bf16 pair (byte + 128 of token 0, token 1):
-      // the fp32 conversion of a byte is exact in its upper half, which one byte
-      // permute per pair moves into place
+      // channel c of the two tokens as one bf16 pair: a signed byte has at most 8
+      // significant bits, so its fp32 conversion (one instruction, sign-extending the
+      // byte) is exact in the upper half, which one byte permute per pair moves into place
       uint32_t vp[CH];
 #pragma unroll
       for (int e = 0; e < NW; ++e) {
-        const uint32_t x0 = vc[pp][0][e] ^ 0x80808080u, x1 = vc[pp][1][e] ^ 0x80808080u;
+        const uint32_t x0 = vc[pp][0][e], x1 = vc[pp][1][e];
 #pragma unroll
         for (int k = 0; k < 4; ++k)
-          vp[4 * e + k] = __builtin_amdgcn_perm(__float_as_uint((float)((x1 >> (8 * k)) & 0xffu)),
-                                                __float_as_uint((float)((x0 >> (8 * k)) & 0xffu)), 0x07060302u);
+          vp[4 * e + k] = __builtin_amdgcn_perm(__float_as_uint((float)(signed char)(x1 >> (8 * k))),
+                                                __float_as_uint((float)(signed char)(x0 >> (8 * k))), 0x07060302u);
       }
       const bool v0 = (p + pp) * kPage + 2 * tg < n && p + pp < p_end;
       const bool v1 = (p + pp) * kPage + 2 * tg + 1 < n && p + pp < p_end;
@@ -577,7 +577,6 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_int8_kernel(
         const float p1 = v1 ? exp2_fast(fmaf(sc[pp][1][hh], kh[hh], nmk[hh])) : 0.f;
         l_run[hh] += p0 + p1;
         const uint32_t ps = pack_bf16x2(p0 * s0, p1 * s1);
-        corr[hh] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(ps), as_bf16x2(0x43004300u), corr[hh], false);
 #pragma unroll
         for (int i = 0; i < CH; ++i)
           acc[hh][i] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(ps), as_bf16x2(vp[i]), acc[hh][i], false);
@@ -606,7 +605,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_int8_kernel(
     const float f = m_run[hh] == -INFINITY ? 0.f : exp2_fast((m_run[hh] - mw) * kh[hh]);
     l_run[hh] = sum_stride8(l_run[hh] * f);
 #pragma unroll
-    for (int i = 0; i < CH; ++i) acc[hh][i] = sum_stride8((acc[hh][i] - corr[hh]) * f);
+    for (int i = 0; i < CH; ++i) acc[hh][i] = sum_stride8(acc[hh][i] * f);
     m_run[hh] = mw == -INFINITY ? -INFINITY : mw * kh[hh];
   }
   if (lane < 8) {
