@@ -27,6 +27,7 @@
 // Phase 2 (decode_merge_kernel): per (sequence, query head) combine the splits:
 // L = log sum_c exp(lse_c), O = sum_c exp(lse_c - L) o_c.
 #include <mutex>
+#include <type_traits>
 
 #include "fa_device.h"
 #include "fa_launch.h"
@@ -485,24 +486,33 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_int8_kernel(
   // as in decode_split_kernel: a page past the split gets empty buffer descriptors
   vec_t ka[PP][2], va[PP][2], kb[PP][2], vb[PP][2];
   float ksa[PP][2], vsa[PP][2], ksb[PP][2], vsb[PP][2];
-  auto fetch = [&](int p0, vec_t (&kd)[PP][2], vec_t (&vd)[PP][2], float (&ksd)[PP][2], float (&vsd)[PP][2]) {
+  // pages p_begin .. p_full - 1 hold 16 tokens of the context each; a sequence's last
+  // page may hold fewer (only in its last split)
+  const int p_full = min(p_end, n / kPage);
+  // fetch pages p0 .. p0 + PP - 1 (those at or past lim get empty descriptors)
+  auto fetch = [&](int p0, int lim, vec_t (&kd)[PP][2], vec_t (&vd)[PP][2], float (&ksd)[PP][2],
+                   float (&vsd)[PP][2]) {
 #pragma unroll
     for (int pp = 0; pp < PP; ++pp) {
       const int p = p0 + pp;
-      const bool valid = p < p_end;
+      const bool valid = p < lim;
       const size_t head = (size_t)page_id_of(lane_pid, min(p, p_end - 1) - p_begin) * Hkv + g;
       load_block<2>(KQ + head * kPage * D, VQ + head * kPage * D, valid ? kPage * D : 0, boff, kd[pp], vd[pp]);
       load_block<2>(KS + head * kPage * NG, VS + head * kPage * NG, valid ? kPage * NG * 4 : 0, soff, ksd[pp],
                     vsd[pp]);
     }
   };
-  auto consume = [&](int p, vec_t (&kc)[PP][2], vec_t (&vc)[PP][2], float (&ksc)[PP][2], float (&vsc)[PP][2]) {
+  // FULL: every token of the pages lies inside the context, so the per-token validity
+  // selects are left out
+  auto consume = [&](auto full, int p, vec_t (&kc)[PP][2], vec_t (&vc)[PP][2], float (&ksc)[PP][2],
+                     float (&vsc)[PP][2]) {
+    constexpr bool FULL = decltype(full)::value;
     float sc[PP][2][HB];  // raw scores (q.k * kscale), -inf past the context
 #pragma unroll
     for (int pp = 0; pp < PP; ++pp)
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        const bool valid = (p + pp) * kPage + 2 * tg + j < n && p + pp < p_end;
+        const bool valid = FULL || ((p + pp) * kPage + 2 * tg + j < n && p + pp < p_end);
         // key byte b as the fp16 value 1024 + (b + 128): the unsigned byte b ^ 0x80
         // becomes the low byte of an fp16 whose high byte is 0x64 (one byte permute per
         // channel pair); the products with fp16 q are exact in the fp32 sums
@@ -567,8 +577,8 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_int8_kernel(
           vp[4 * e + k] = __builtin_amdgcn_perm(__float_as_uint((float)(signed char)(x1 >> (8 * k))),
                                                 __float_as_uint((float)(signed char)(x0 >> (8 * k))), 0x07060302u);
       }
-      const bool v0 = (p + pp) * kPage + 2 * tg < n && p + pp < p_end;
-      const bool v1 = (p + pp) * kPage + 2 * tg + 1 < n && p + pp < p_end;
+      const bool v0 = FULL || ((p + pp) * kPage + 2 * tg < n && p + pp < p_end);
+      const bool v1 = FULL || ((p + pp) * kPage + 2 * tg + 1 < n && p + pp < p_end);
       // invalid tokens (possibly NaN scales) contribute exactly nothing
       const float s0 = v0 ? vsc[pp][0] : 0.f, s1 = v1 ? vsc[pp][1] : 0.f;
 #pragma unroll
@@ -584,17 +594,23 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_int8_kernel(
     }
   };
 
+  // wave w takes pages p_begin + PP (w + 4 i): whole pages in the loop, then the
+  // sequence's partial last page (or the pages of a partial group) after it
   constexpr int kStride = PP * kDecWaves;
   int p = p_begin + PP * w;
-  if (p < p_end) fetch(p, ka, va, ksa, vsa);
-  while (p < p_end) {
-    fetch(p + kStride, kb, vb, ksb, vsb);
-    consume(p, ka, va, ksa, vsa);
+  if (p + PP <= p_full) fetch(p, p_full, ka, va, ksa, vsa);
+  while (p + PP <= p_full) {
+    fetch(p + kStride, p_full, kb, vb, ksb, vsb);
+    consume(std::true_type{}, p, ka, va, ksa, vsa);
     p += kStride;
-    if (p >= p_end) break;
-    fetch(p + kStride, ka, va, ksa, vsa);
-    consume(p, kb, vb, ksb, vsb);
+    if (p + PP > p_full) break;
+    fetch(p + kStride, p_full, ka, va, ksa, vsa);
+    consume(std::true_type{}, p, kb, vb, ksb, vsb);
     p += kStride;
+  }
+  if (p < p_end) {
+    fetch(p, p_end, ka, va, ksa, vsa);
+    consume(std::false_type{}, p, ka, va, ksa, vsa);
   }
 
   // bring the 8 token-pair lanes to a common max, remove the byte offset, combine the
