@@ -663,9 +663,35 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void fwd_bf16_kernel(
   __syncthreads();
 
   int ndone = 0;  // tiles this wave has processed (EXT)
+  int t_start = t_begin;
+  if constexpr (PAGED) {
+    // Causal in positions: every row of the block sees every key of the tiles below
+    // t_m, so those tiles run through the unmasked body in a loop of their own.  With
+    // both bodies in one loop the register allocator kept the O accumulators in two
+    // places and copied them in and out on every unmasked tile of this instantiation.
+    static_assert(!PAGED || CAUSAL, "the paged forward is causal");
+    const int t_m = min(ntiles, (poff + qb * kBR + 1) / LY::BC);
+    const int t_split = t_begin + max(0, (t_m - t_begin) / kStages) * kStages;
+    for (int t0 = t_begin; t0 < t_split; t0 += kStages) {
+#pragma unroll
+      for (int u = 0; u < kStages; ++u) {
+        const int t = t0 + u;
+        const int j0 = t * LY::BC;
+        if (t + kStages - 1 < ntiles)
+          copy_tile_paged<D>(smem, K, V, trow, Nk, num_pages, Hkv, g, j0 + kAhead, (u + kStages - 1) % kStages, w,
+                             lane);
+        debug_copy_fence();
+        process_tile<D, false, false>(st, smem + u * LY::TBYTES, smem + (kStages + u) * LY::TBYTES, koff, voff,
+                                      qrowp - j0 - 4 * hi, l32, c);
+        wait_vmem_tiles<kLoadsPerTile>(max(0, min(kStages - 2, ntiles - 2 - t)));
+        __syncthreads();
+      }
+    }
+    t_start = t_split;
+  }
   // The loop is unrolled by kStages so every slot index, and with it every LDS
   // address offset, is a compile-time constant.
-  for (int t0 = t_begin; t0 < ntiles; t0 += kStages) {
+  for (int t0 = t_start; t0 < ntiles; t0 += kStages) {
 #pragma unroll
     for (int u = 0; u < kStages; ++u) {
       const int t = t0 + u;
