@@ -465,6 +465,48 @@ __device__ __forceinline__ void copy_tile_paged(uint8_t* smem, const uint16_t* k
   }
 }
 
+// Page ids of one K/V tile of the paged cache (keys j0 .. j0 + BC - 1), one per lane:
+// lane i holds the table entry of page j0 / 16 + i.  One vector load through a buffer
+// descriptor spanning the sequence's pages with tokens, so lanes past them read 0.
+// The loop loads the ids a tile ahead of the copy that uses them, so the copy does not
+// wait for a page-table read.
+template <int D>
+__device__ __forceinline__ int load_tile_page_ids(const int32_t* trow, int nk, int j0, int lane) {
+  const uint32_t bytes = (uint32_t)((nk + 15) / 16) * 4;
+  const auto rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<int32_t*>(trow), (short)0, bytes, 0x00020000);
+  return (int)__builtin_amdgcn_raw_buffer_load_b32(rs, (j0 / 16 + lane) * 4, 0, 0);
+}
+
+// copy_tile_paged with the tile's page ids already in a register (load_tile_page_ids).
+template <int D>
+__device__ __forceinline__ void copy_tile_paged_ids(uint8_t* smem, const uint16_t* kpool, const uint16_t* vpool,
+                                                    int idv, int nk, int num_pages, int Hkv, int g, int j0, int buf,
+                                                    int w, int lane) {
+  using LY = Lay<D>;
+  uint8_t* kb = smem + buf * LY::TBYTES;
+  uint8_t* vb = smem + (kStages + buf) * LY::TBYTES;
+#pragma unroll
+  for (int i = 0; i < LY::BPW; ++i) {
+    const int blk = w + kWaves * i;
+    const int r0 = blk * LY::RPB;
+    const int tp = (j0 + r0) / 16;
+    const int valid = __builtin_amdgcn_readfirstlane(min(max(nk - tp * 16, 0), 16));
+    const int id = __builtin_amdgcn_readlane(idv, r0 / 16);  // j0 is a multiple of 16
+    const int pid = (unsigned)id < (unsigned)num_pages ? id : num_pages - 1;
+    const size_t head = ((size_t)pid * Hkv + g) * 16 * D;
+    const auto krs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(kpool + head), (short)0,
+                                                       (uint32_t)valid * LY::ROWB, 0x00020000);
+    const auto vrs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(vpool + head), (short)0,
+                                                       (uint32_t)valid * LY::ROWB, 0x00020000);
+    const int r = r0 + lane / LY::CPR;
+    const int pc = lane % LY::CPR;
+    const uint32_t ko = (r % 16) * LY::ROWB + ((pc ^ LY::swz_k(r)) << 4);
+    const uint32_t vo = (r % 16) * LY::ROWB + ((pc ^ LY::swz_v(r)) << 4);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (FA_LDS void*)(kb + blk * 1024), 16, ko, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (FA_LDS void*)(vb + blk * 1024), 16, vo, 0, 0, 0);
+  }
+}
+
 template <int D, bool CAUSAL, bool EXT, bool PAGED>
 __global__ __launch_bounds__(kThreads, 8 / kWaves) void fwd_bf16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
@@ -659,6 +701,9 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void fwd_bf16_kernel(
       else
         copy_tile<D>(smem, kbase, vbase, head_bytes, kcp, vcp, (rev ? ntiles - 1 - p : t_begin + p) * LY::BC, p, w);
     }
+  // paged: the page ids of the first tile copied inside the loops
+  int idv = 0;
+  if constexpr (PAGED) idv = load_tile_page_ids<D>(trow, Nk, (t_begin + kStages - 1) * LY::BC, lane);
   wait_vmem_tiles<kLoadsPerTile>(min(kStages - 2, ntiles - 1 - t_begin));  // the first tile has landed
   __syncthreads();
 
@@ -677,9 +722,11 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void fwd_bf16_kernel(
       for (int u = 0; u < kStages; ++u) {
         const int t = t0 + u;
         const int j0 = t * LY::BC;
-        if (t + kStages - 1 < ntiles)
-          copy_tile_paged<D>(smem, K, V, trow, Nk, num_pages, Hkv, g, j0 + kAhead, (u + kStages - 1) % kStages, w,
-                             lane);
+        if (t + kStages - 1 < ntiles) {
+          copy_tile_paged_ids<D>(smem, K, V, idv, Nk, num_pages, Hkv, g, j0 + kAhead, (u + kStages - 1) % kStages, w,
+                                 lane);
+          idv = load_tile_page_ids<D>(trow, Nk, j0 + kAhead + LY::BC, lane);  // covered by the end-of-tile wait
+        }
         debug_copy_fence();
         process_tile<D, false, false>(st, smem + u * LY::TBYTES, smem + (kStages + u) * LY::TBYTES, koff, voff,
                                       qrowp - j0 - 4 * hi, l32, c);
@@ -698,10 +745,11 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void fwd_bf16_kernel(
       if (t >= ntiles) break;
       const int j0 = rev ? (ntiles - 1 - (t - t_begin)) * LY::BC : t * LY::BC;
       if (t + kStages - 1 < ntiles) {
-        if constexpr (PAGED)
-          copy_tile_paged<D>(smem, K, V, trow, Nk, num_pages, Hkv, g, rev ? j0 - kAhead : j0 + kAhead, (u + kStages - 1) % kStages, w,
-                             lane);
-        else
+        if constexpr (PAGED) {
+          copy_tile_paged_ids<D>(smem, K, V, idv, Nk, num_pages, Hkv, g, j0 + kAhead, (u + kStages - 1) % kStages, w,
+                                 lane);
+          idv = load_tile_page_ids<D>(trow, Nk, j0 + kAhead + LY::BC, lane);  // covered by the end-of-tile wait
+        } else
           copy_tile<D>(smem, kbase, vbase, head_bytes, kcp, vcp, rev ? j0 - kAhead : j0 + kAhead,
                        (u + kStages - 1) % kStages, w);
       }
