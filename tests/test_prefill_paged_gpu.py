@@ -39,6 +39,11 @@ CASES = [
     (2, 32, 8, 128, 300, (300, 5000)),
     (2, 2, 2, 128, 513, (513, 2049)),
     (3, 8, 1, 64, 64, (64, 65, 1024)),
+    # the kernel runs the tiles below a block's causal boundary in a loop of their own
+    # (an even number of them) and the rest in the general loop: boundaries at tiles 1,
+    # 2, 5 and 6 (64-key tiles), so the first loop is empty, even and odd-rounded
+    (2, 8, 2, 128, 300, (363, 427)),
+    (2, 4, 2, 64, 200, (327, 711)),
 ]
 
 
