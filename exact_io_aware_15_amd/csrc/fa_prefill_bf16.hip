@@ -9,7 +9,8 @@
 // Work decomposition: one item per (256-row query block, query head, batch), taken by
 // a workgroup of 8 waves (two per SIMD); the plain forward runs one persistent
 // workgroup per compute unit over a static list of items (fwd_bf16_persistent_kernel),
-// the windowed, ALiBi and paged forms one workgroup per item.  Each wave owns 32 query rows and keeps their Q
+// the windowed, ALiBi and paged forms one workgroup per item, and the split-K form one
+// workgroup per chunk of an item's key tiles.  Each wave owns 32 query rows and keeps their Q
 // fragments in registers for the whole pass.  K/V are streamed in tiles of 64
 // keys (128 at d = 64) through two LDS buffers: the next tile is copied
 // HBM -> LDS by 128-bit buffer loads with the LDS-destination bit (no staging
