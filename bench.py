@@ -23,6 +23,7 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+import re
 import json
 import os
 import sys
@@ -203,11 +204,19 @@ def output_check(O, L, Oref, Lref, tol_o=1e-2, tol_l=1e-3):
             "pass": bool(np.all(np.isfinite(O)) and faithful.all() and el <= tol_l)}
 
 
+def _code_only(text):
+    """Source text without comments and with whitespace runs collapsed, so that a digest
+    changes with the code and not with its comments."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def source_digest(files):
     h = hashlib.sha256()
     for f in files:
-        with open(os.path.join(ROOT, "exact_io_aware_15_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "exact_io_aware_15_amd", "csrc", f), encoding="utf-8") as fh:
+            h.update(_code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 
