@@ -191,6 +191,8 @@ DECODE_SMALL = [
     (3, 16, 2, 128, (5, 70, 1600)),   # 8 query heads per K/V head
     (3, 8, 1, 64, (33, 1, 64)),       # multi-query
     (2, 2, 1, 128, (16384, 9999)),
+    (3, 6, 2, 128, (40, 17, 2100)),   # 3 query heads per K/V head: one of 4 head slots idle
+    (2, 12, 2, 64, (300, 4097)),      # 6 per K/V head: two workgroups, the second half full
 ]
 
 

@@ -44,6 +44,7 @@ CASES = [
     # 2, 5 and 6 (64-key tiles), so the first loop is empty, even and odd-rounded
     (2, 8, 2, 128, 300, (363, 427)),
     (2, 4, 2, 64, 200, (327, 711)),
+    (2, 6, 2, 128, 100, (100, 700)),  # 3 query heads per K/V head
 ]
 
 
