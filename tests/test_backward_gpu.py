@@ -141,6 +141,8 @@ SMALL = [
     (2, 8, 1, 129, 128, True),
     (1, 2, 2, 513, 64, True),
     (1, 1, 1, 640, 128, True),
+    (1, 6, 2, 200, 128, True),   # 3 query heads per K/V head
+    (1, 5, 1, 150, 64, False),   # 5 query heads on one K/V head
 ]
 
 

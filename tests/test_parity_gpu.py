@@ -59,6 +59,8 @@ SMALL = [
     # epilogue instead of during the last tile): 288 items each
     (1, 96, 8, 576, 128, True, "bf16"),
     (2, 48, 48, 640, 64, True, "bf16"),
+    (2, 6, 2, 450, 128, True, "bf16"),   # 3 query heads per K/V head
+    (1, 5, 1, 200, 64, False, "bf16"),   # 5 query heads on one K/V head
     (1, 1, 1, 256, 64, False, "f32"),
     (1, 2, 1, 130, 128, True, "f32"),
     (2, 2, 2, 65, 64, True, "f32"),
