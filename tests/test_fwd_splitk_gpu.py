@@ -24,6 +24,7 @@ SPLIT_SHAPES = [
     (2, 2, 2, 700, 128, True),
     (1, 1, 1, 300, 64, True),
     (1, 1, 1, 64, 128, False),      # one tile: nothing to split
+    (1, 6, 2, 1800, 128, True),     # 3 query heads per K/V head
 ]
 
 

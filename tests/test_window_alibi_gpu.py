@@ -44,6 +44,7 @@ SMALL = [
     (1, 2, 1, 130, 64, True, 500, True),     # window wider than the sequence
     (1, 4, 4, 333, 128, True, 0, True),      # ALiBi only
     (2, 4, 2, 190, 64, False, 0, True),      # non-causal ALiBi: -m |i - j|
+    (1, 6, 2, 420, 128, True, 150, True),    # 3 query heads per K/V head
 ]
 
 
